@@ -1,0 +1,174 @@
+"""ctypes binding of libattn.so (argument marshalling only).
+
+Every step of the attention path runs in the library's HIP kernels; this
+module checks that tensors are on the GPU with the expected dtype and layout,
+reads their sizes, and passes raw device pointers and the current HIP stream.
+There is no fallback: if the library is missing or a tensor is not on the
+device, the call raises.
+"""
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+_LOCK = threading.Lock()
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_HIP = 3
+ATTN_BF16 = 0
+ATTN_F32 = 1
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+def library_path():
+    return os.environ.get("ATTN_LIBRARY", os.path.join(_HERE, "libattn.so"))
+
+
+def load_library():
+    """Load libattn.so once. torch is imported first so that the library binds to the
+    HIP runtime that torch already has in the process."""
+    global _LIB
+    with _LOCK:
+        if _LIB is not None:
+            return _LIB
+        import torch  # noqa: F401  (HIP runtime first)
+        path = library_path()
+        if not os.path.exists(path):
+            raise AttnError(-1, "libattn.so not found at %s: build it with __graft_entry__.build()" % path)
+        lib = ctypes.CDLL(path)
+        c_int, c_float, c_void_p, c_size_t = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+        lib.attn_abi_version.restype = c_int
+        lib.attn_abi_version.argtypes = []
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [c_int]
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_prefill_fwd.restype = c_int
+        lib.attn_prefill_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                         c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                         c_float, c_int, c_float, c_void_p, c_void_p]
+        lib.attn_decode_workspace_bytes.restype = c_size_t
+        lib.attn_decode_workspace_bytes.argtypes = [c_int] * 7
+        lib.attn_decode_fwd.restype = c_int
+        lib.attn_decode_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                        c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                        c_float, c_int, c_float, c_void_p,
+                                        c_void_p, c_int, c_int, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_int, ctypes.c_int64,
+                                        c_void_p, c_size_t, c_void_p]
+        _LIB = lib
+        return lib
+
+
+def attn_abi_version():
+    return load_library().attn_abi_version()
+
+
+def attn_status_string(status):
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != ATTN_OK:
+        lib = load_library()
+        msg = lib.attn_last_error().decode() or lib.attn_status_string(status).decode()
+        raise AttnError(status, msg)
+
+
+def _ptr(t, name, dtype=None, allow_none=False):
+    import torch
+    if t is None:
+        if allow_none:
+            return None
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be on the GPU (got %s)" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _odtype(o):
+    import torch
+    if o.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if o.dtype == torch.float32:
+        return ATTN_F32
+    raise AttnError(ATTN_ERR_INVALID_ARG, "o must be bfloat16 or float32")
+
+
+def attn_prefill_fwd(q, k, v, o, lse=None, *, scale, causal=False, softcap=0.0, sinks=None, stream=None):
+    """q [B,Sq,Hq,dk], k [B,Sk,Hkv,dk], v [B,Sk,Hkv,dv] bf16; o [B,Sq,Hq,dv] bf16|fp32;
+    lse optional fp32 [B,Hq,Sq]; sinks optional fp32 [Hq]. Enqueued on `stream`
+    (default: torch's current stream)."""
+    import torch
+    lib = load_library()
+    B, Sq, Hq, dk = q.shape
+    _, Sk, Hkv, _ = k.shape
+    dv = v.shape[3]
+    st = lib.attn_prefill_fwd(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                              _ptr(v, "v", torch.bfloat16), _ptr(o, "o"), _odtype(o),
+                              _ptr(lse, "lse", torch.float32, True),
+                              B, Hq, Hkv, Sq, Sk, dk, dv, float(scale), int(bool(causal)), float(softcap),
+                              _ptr(sinks, "sinks", torch.float32, True), _stream(stream))
+    _check(st)
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk_max, dk, dv):
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk_max, dk, dv))
+
+
+def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=False, softcap=0.0,
+                    sinks=None, block_table=None, seq_lens=None, row_index=None, key_pos=None,
+                    q_pos=None, kv_row_stride=0, Hkv=None, dk=None, dv=None, stream=None):
+    """Paged mode: k_cache [n_blocks,Hkv,bs,dk], v_cache [n_blocks,Hkv,bs,dv], block_table
+    [B,max_blocks] int32, seq_lens [B] int32. Gathered mode: k_cache / v_cache are row
+    arrays (any shape; dk, dv and kv_row_stride given), row_index [B,n_sel] int32,
+    key_pos [B,n_sel] fp32, q_pos [B] int32. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv]."""
+    import torch
+    lib = load_library()
+    B, Sq, Hq, qdk = q.shape
+    paged = block_table is not None
+    if paged:
+        Hkv_, bs, dk_ = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+        dv_ = v_cache.shape[3]
+        Hkv, dk, dv = Hkv_, dk_, dv_
+        max_blocks = block_table.shape[1]
+        n_sel = 0
+    else:
+        bs, max_blocks = 0, 0
+        n_sel = row_index.shape[1] if row_index is not None else 0
+        Hkv = 1 if Hkv is None else Hkv
+        dk = qdk if dk is None else dk
+        dv = o.shape[3] if dv is None else dv
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_decode_fwd(_ptr(q, "q", torch.bfloat16), _ptr(k_cache, "k_cache", torch.bfloat16),
+                             _ptr(v_cache, "v_cache", torch.bfloat16), _ptr(o, "o"), _odtype(o),
+                             B, Hq, Hkv, Sq, int(Sk_max), dk, dv, float(scale), int(bool(causal)),
+                             float(softcap), _ptr(sinks, "sinks", torch.float32, True),
+                             _ptr(block_table, "block_table", torch.int32, True), bs, max_blocks,
+                             _ptr(seq_lens, "seq_lens", torch.int32, True),
+                             _ptr(row_index, "row_index", torch.int32, True),
+                             _ptr(key_pos, "key_pos", torch.float32, True),
+                             _ptr(q_pos, "q_pos", torch.int32, True), n_sel, int(kv_row_stride),
+                             _ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(st)

@@ -1,0 +1,150 @@
+/*
+ * attn.h - C ABI of libattn.so: fused scaled-dot-product attention on MI355X (gfx950).
+ *
+ * The operation (per batch b, query i, query head h):
+ *
+ *     x_j  = scale * <q_i, k_j>                  raw dot product, scaled afterwards
+ *     x_j  = softcap * tanh(x_j / softcap)       only when softcap != 0
+ *     keys excluded by the mask are dropped
+ *     o_i  = sum_j e^{x_j} v_j / (sum_j e^{x_j} + e^{sink_h})     (sink term only with sinks)
+ *
+ * computed tile by tile with a running max and running sum, so no score matrix
+ * is ever written to memory. Sources: the fa.metal tensor kernel on the
+ * "ggml-metal: FA tensor path: gate to the (256, 256) shape" page (score step:
+ * scale, softcap, mask; online softmax; final block "sinks, O /= S" with a
+ * zero-sum row written as 0; GQA head map h / (Hq / Hkv)); the "UMMA FMHA"
+ * page, "Key lessons learned" (the matrix product is unscaled, the scale is
+ * applied afterwards); the "MLA Decode Attention Kernel API Reference" page,
+ * Background and parameters (rows gathered from a paged cache by a row list,
+ * causal mask from each key's absolute position against the token's).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; inputs are
+ *     read only. The library never allocates, frees or synchronises on the
+ *     call path: it validates on the host, enqueues kernels on `stream` and
+ *     returns. Outputs are valid once the stream has executed the work.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - bf16 tensors are IEEE bfloat16 bit patterns; fp32 is IEEE binary32.
+ *   - All argument checks run before any HIP call. On an error status nothing
+ *     has been enqueued and the outputs are untouched (ATTN_ERR_HIP: a launch
+ *     failed; outputs are then undefined). attn_last_error() gives a message.
+ *   - Thread-safe; the library holds no state across calls.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv) (contiguous groups);
+ *     Hq must be a multiple of Hkv.
+ *   - Causal masking is bottom-right aligned: query i of a sequence with Sq
+ *     queries and Sk keys sits at absolute position Sk - Sq + i and sees keys
+ *     j <= Sk - Sq + i. A row that sees no key (and has no sink) is written
+ *     as 0 with lse = -inf; with a sink but no key it is 0 as well.
+ *   - sinks (optional, NULL = none): fp32 [Hq], one raw logit per query head,
+ *     not scaled and not softcapped; it joins the softmax denominator and adds
+ *     nothing to the numerator.
+ *   - Supported (dk, dv): (16,16) (32,32) (64,64) (96,96) (128,128) (192,192)
+ *     (256,256) (192,128) for prefill and paged decode; (576,512) for gathered
+ *     decode. Other legal pairs return ATTN_ERR_UNSUPPORTED.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,   /* NULL required pointer, non-positive size, Hq % Hkv != 0, ... */
+    ATTN_ERR_UNSUPPORTED = 2,   /* legal but not built: (dk, dv) pair, mode combination */
+    ATTN_ERR_HIP = 3            /* a HIP launch failed */
+} attn_status;
+
+typedef enum attn_dtype {
+    ATTN_BF16 = 0,
+    ATTN_F32 = 1
+} attn_dtype;
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+/* Static description of a status code. */
+const char* attn_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/*
+ * Prefill (dense) attention.
+ *   q     bf16 [B, Sq, Hq, dk]   contiguous
+ *   k     bf16 [B, Sk, Hkv, dk]  contiguous
+ *   v     bf16 [B, Sk, Hkv, dv]  contiguous
+ *   o     [B, Sq, Hq, dv] contiguous, element type o_dtype (ATTN_BF16 or ATTN_F32);
+ *         bf16 results are rounded to nearest even from the fp32 result.
+ *   lse   optional fp32 [B, Hq, Sq] (NULL = not written): natural-log
+ *         log-sum-exp of the row's live scores and sink (-inf if none).
+ *   scale multiplies the raw dot product (typically 1/sqrt(dk)); must be finite and > 0.
+ *   causal 0/1; softcap >= 0 (0 = off); sinks optional fp32 [Hq].
+ * Accumulation is fp32; the probabilities feed the second product as bf16.
+ */
+attn_status attn_prefill_fwd(const void* q, const void* k, const void* v,
+                             void* o, int o_dtype, float* lse,
+                             int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv,
+                             float scale, int causal, float softcap, const float* sinks,
+                             void* stream);
+
+/*
+ * Workspace (bytes) that attn_decode_fwd needs for these sizes: the split-KV
+ * partial results (fp32 output rows plus running max and sum per split).
+ * Sk_max is the largest sequence length (paged mode) or n_sel (gathered mode).
+ * Returns 0 for sizes that attn_decode_fwd would reject.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv);
+
+/*
+ * Decode attention: Sq query rows per sequence (Sq = 1 is the single-token
+ * case) against a KV cache read in one of two modes. The keys are split into
+ * fixed-size ranges processed in parallel, then merged by log-sum-exp.
+ *
+ *   q   bf16 [B, Sq, Hq, dk] contiguous;   o [B, Sq, Hq, dv] of type o_dtype.
+ *
+ * Paged mode (block_table != NULL, row_index == NULL):
+ *   k_cache bf16 [n_blocks, Hkv, block_size, dk], v_cache bf16 [n_blocks, Hkv, block_size, dv]
+ *   block_table int32 [B, max_blocks_per_seq]: logical key j of sequence b is
+ *     slot j % block_size of physical block block_table[b, j / block_size];
+ *   seq_lens int32 [B] on the device, each in [0, Sk_max]; sequence b has keys
+ *     [0, seq_lens[b]). block_size must be 16, 32, 64 or 128 (multiple of 16).
+ *   The caller guarantees table entries for j < seq_lens[b] are valid blocks.
+ *
+ * Gathered mode (row_index != NULL, block_table == NULL): Hkv must be 1 and Sq 1.
+ *   k_cache, v_cache bf16 row arrays with a common row stride kv_row_stride
+ *     (elements, multiple of 8): the key of row r is k_cache[r*stride .. +dk),
+ *     its value v_cache[r*stride .. +dv) (v_cache may alias k_cache, e.g. the
+ *     value being the row's first dv columns).
+ *   row_index int32 [B, n_sel]: the rows token b attends to (each valid);
+ *   key_pos  fp32  [B, n_sel]: absolute position of each selected key;
+ *   q_pos    int32 [B]: position of token b. With causal, key j is live iff
+ *     key_pos[b, j] <= q_pos[b]; without causal every selected key is live.
+ *   Sk_max must equal n_sel.
+ *
+ *   workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes,
+ *     16-byte aligned, owned by the caller; contents on entry do not matter.
+ *   Two calls that share a workspace must be ordered on one stream.
+ */
+attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                            void* o, int o_dtype,
+                            int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv,
+                            float scale, int causal, float softcap, const float* sinks,
+                            const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                            const int32_t* seq_lens,
+                            const int32_t* row_index, const float* key_pos, const int32_t* q_pos,
+                            int n_sel, int64_t kv_row_stride,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,57 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pin set catches every one of them. This shows the pins constrain each part
+of the definition: the scale, the softcap, the sink term, the causal alignment,
+the GQA head map, the value operand, the lse, the paged and gathered indexing."""
+
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+from oracle_pins import PINS
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.py")
+
+MUTATIONS = {
+    "dropped_scale": ("x = (qrows @ keys.T) * scale", "x = (qrows @ keys.T)"),
+    "softcap_without_division": ("np.tanh(x / softcap)", "np.tanh(x)"),
+    "sink_sign": ("np.exp(float(sink) - m_safe)", "np.exp(m_safe - float(sink))"),
+    "sink_left_out": ("Z = Z + np.exp(float(sink) - m_safe)", "Z = Z"),
+    "causal_top_left": ("live = _causal_live(rows + (Sk - Sq), Sk)", "live = _causal_live(rows, Sk)"),
+    "causal_strict": ("return j[None, :] <= np.asarray(q_positions)[:, None]",
+                      "return j[None, :] < np.asarray(q_positions)[:, None]"),
+    "gqa_modulo": ("g = h // group\n            sink", "g = h % Hkv\n            sink"),
+    "keys_as_values": ("num = e @ values", "num = e @ keys[:, :dv]"),
+    "lse_without_log": ("m_safe + np.log(np.where(Z > 0, Z, 1.0))", "m_safe + np.where(Z > 0, Z, 1.0)"),
+    "empty_row_not_zero": ("o[ok] = num[ok] / Z[ok, None]", "o[:] = num / np.where(Z > 0, Z, 1.0)[:, None] + (~ok)[:, None]"),
+    "paged_slot_index": ("slot = j % bs", "slot = (j + 1) % bs"),
+    "paged_block_index": ("phys = block_table[b, j // bs]", "phys = block_table[b, j % block_table.shape[1]]"),
+    "gathered_strict_position": ("(key_pos[t] <= float(q_pos[t]))", "(key_pos[t] < float(q_pos[t]))"),
+    "gathered_value_rows": ("V = _as_f64(v_rows[r])", "V = _as_f64(v_rows[np.sort(r)])"),
+    "max_ignores_mask": ("x = np.where(live, x, -np.inf)", "x = np.where(live, x, -1e3)"),
+}
+
+
+def _mutant(old, new):
+    with open(ORACLE_SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation anchor not found exactly once: %r" % old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    mod = _mutant(*MUTATIONS[name])
+    caught = []
+    for pname, pin in PINS.items():
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pname)
+        except Exception:  # a crash also exposes the mistake
+            caught.append(pname + "(error)")
+    assert caught, "no pin caught the planted mistake %s" % name
