@@ -1,0 +1,179 @@
+// C ABI of libattn.so: argument validation on the host, then kernel launches.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing; see include/attn.h for the contract of each entry point.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "attn_launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+attn_status ok() {
+    g_last_error[0] = '\0';
+    return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+attn_status check_common(int B, int Hq, int Hkv, int Sq, int dk, int dv, float scale, float softcap,
+                         int o_dtype) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || dk <= 0 || dv <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d Sq=%d dk=%d dv=%d)", B, Hq,
+                    Hkv, Sq, dk, dv);
+    if (Hq % Hkv != 0) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (!(std::isfinite(scale) && scale > 0.f))
+        return fail(ATTN_ERR_INVALID_ARG, "scale must be finite and positive");
+    if (!(std::isfinite(softcap) && softcap >= 0.f))
+        return fail(ATTN_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0 = off)");
+    if (o_dtype != ATTN_BF16 && o_dtype != ATTN_F32)
+        return fail(ATTN_ERR_INVALID_ARG, "o_dtype must be ATTN_BF16 or ATTN_F32");
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_INVALID_ARG: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case ATTN_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+                             int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale, int causal,
+                             float softcap, const float* sinks, void* stream) {
+    if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o are required");
+    attn_status st = check_common(B, Hq, Hkv, Sq, dk, dv, scale, softcap, o_dtype);
+    if (st != ATTN_OK) return st;
+    if (Sk <= 0) return fail(ATTN_ERR_INVALID_ARG, "Sk must be positive (got %d)", Sk);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (!attn::prefill_supported(dk, dv))
+        return fail(ATTN_ERR_UNSUPPORTED, "prefill (dk, dv) = (%d, %d) is not built", dk, dv);
+    const double rows = (double)B * Sq * Hq;
+    if ((double)B * ((Sq + 127) / 128) * Hq > 2147483647.0 || rows * dv > 9.0e18)
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+
+    attn::PrefillArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.sinks = sinks;
+    a.o_f32 = o_dtype == ATTN_F32;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.dk = dk;
+    a.dv = dv;
+    a.scale = scale;
+    a.causal = causal ? 1 : 0;
+    a.softcap = softcap;
+    hipError_t e = attn::launch_prefill(a, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk_max < 0 || dk <= 0 || dv <= 0 || Hq % Hkv != 0) return 0;
+    return attn::decode_plan(B, Hq, Hkv, Sq, Sk_max, dk, dv).ws_bytes;
+}
+
+attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype, int B,
+                            int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv, float scale, int causal,
+                            float softcap, const float* sinks, const int32_t* block_table, int block_size,
+                            int max_blocks_per_seq, const int32_t* seq_lens, const int32_t* row_index,
+                            const float* key_pos, const int32_t* q_pos, int n_sel, int64_t kv_row_stride,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o are required");
+    attn_status st = check_common(B, Hq, Hkv, Sq, dk, dv, scale, softcap, o_dtype);
+    if (st != ATTN_OK) return st;
+    const bool paged = block_table != nullptr;
+    const bool gathered = row_index != nullptr;
+    if (paged == gathered)
+        return fail(ATTN_ERR_INVALID_ARG, "exactly one of block_table (paged) and row_index (gathered) must be given");
+    if (Sk_max < 0) return fail(ATTN_ERR_INVALID_ARG, "Sk_max must be >= 0");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
+        return fail(ATTN_ERR_INVALID_ARG, "q, caches and o must be 16-byte aligned");
+    if (paged) {
+        if (!seq_lens) return fail(ATTN_ERR_INVALID_ARG, "paged mode needs seq_lens");
+        if (block_size != 16 && block_size != 32 && block_size != 64 && block_size != 128)
+            return fail(ATTN_ERR_INVALID_ARG, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
+        if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < Sk_max)
+            return fail(ATTN_ERR_INVALID_ARG, "max_blocks_per_seq * block_size must cover Sk_max");
+        if (Sq * (Hq / Hkv) > 32)
+            return fail(ATTN_ERR_UNSUPPORTED, "paged decode needs Sq * (Hq / Hkv) <= 32 (got %d)", Sq * (Hq / Hkv));
+    } else {
+        if (!key_pos || !q_pos) return fail(ATTN_ERR_INVALID_ARG, "gathered mode needs key_pos and q_pos");
+        if (Hkv != 1 || Sq != 1) return fail(ATTN_ERR_INVALID_ARG, "gathered mode needs Hkv == 1 and Sq == 1");
+        if (n_sel <= 0 || n_sel != Sk_max) return fail(ATTN_ERR_INVALID_ARG, "gathered mode needs n_sel == Sk_max > 0");
+        if (kv_row_stride < dk || kv_row_stride < dv || kv_row_stride % 8 != 0)
+            return fail(ATTN_ERR_INVALID_ARG, "kv_row_stride must be a multiple of 8 and >= dk, dv");
+    }
+    if (!attn::decode_supported(dk, dv, gathered))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s decode (dk, dv) = (%d, %d) is not built", gathered ? "gathered" : "paged",
+                    dk, dv);
+    const attn::DecodePlan pl = attn::decode_plan(B, Hq, Hkv, Sq, Sk_max, dk, dv);
+    if (!workspace || workspace_bytes < pl.ws_bytes)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", pl.ws_bytes, workspace_bytes);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    attn::DecodeArgs a;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.o = o;
+    a.sinks = sinks;
+    a.o_f32 = o_dtype == ATTN_F32;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = Sq;
+    a.Sk_max = Sk_max;
+    a.dk = dk;
+    a.dv = dv;
+    a.scale = scale;
+    a.causal = causal ? 1 : 0;
+    a.softcap = softcap;
+    a.block_table = block_table;
+    a.block_size = block_size;
+    a.max_blocks = max_blocks_per_seq;
+    a.seq_lens = seq_lens;
+    a.row_index = row_index;
+    a.key_pos = key_pos;
+    a.q_pos = q_pos;
+    a.n_sel = n_sel;
+    a.row_stride = kv_row_stride;
+    a.workspace = workspace;
+    hipError_t e = attn::launch_decode(a, pl, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

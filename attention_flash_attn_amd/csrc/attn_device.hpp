@@ -1,0 +1,73 @@
+// Device helpers shared by the attention kernels (gfx950 / CDNA4, wave64).
+//
+// MFMA operand maps used throughout (verified on the hardware):
+//   v_mfma_f32_32x32x16_bf16  A[32 x 16], B[16 x 32], D[32 x 32]
+//     lane l supplies A[row l%32][k (l/32)*8 + e] and B[k (l/32)*8 + e][col l%32], e = 0..7
+//     lane l holds   D[row (i/4)*8 + (l/32)*4 + i%4][col l%32] in accumulator i = 0..15
+//   ds_read_b64_tr_b16 (per 16-lane group): lane 4r + c points at 4 bf16 of row r,
+//     columns 4c..4c+3 of a 4 x 16 block; lane i receives column i, rows 0..3.
+//   v_permlane32_swap(x, x) returns {x[l%32], x[l%32 + 32]} in some order on
+//     every lane, so max/sum of the pair combines the two half-waves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum of a value across the two half-waves (lanes l and l^32).
+__device__ __forceinline__ float halfwave_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halfwave_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Round two floats to bf16 (nearest even) and pack them, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Transposing LDS read: 4 bf16 (one column of a 4 x 16 block per lane, see above).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (ATTN_LDS bf16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+
+// 16-byte chunk swizzle inside an LDS row of nch chunks. Rows r..r+7 map a
+// given chunk to 8 different 16-byte bank groups (conflict-free 128-bit reads
+// of one column chunk by consecutive rows), and rows 4a..4a+3 map an aligned
+// chunk pair to 4 different 32-byte bank groups (conflict-free transposing
+// reads of 4 rows x 16 columns).
+template <int NCH>
+__device__ __forceinline__ int swz(int r) {
+    constexpr int mask = (NCH % 8 == 0) ? 7 : (NCH % 4 == 0) ? 3 : (NCH % 2 == 0) ? 1 : 0;
+    return (((r & 3) << 1) | ((r >> 2) & 1)) & mask;
+}
+
+}  // namespace attn

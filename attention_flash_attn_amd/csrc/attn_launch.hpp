@@ -1,0 +1,65 @@
+// Host-side launch interface between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const float* sinks;
+    int o_f32;
+    int B, Hq, Hkv, Sq, Sk, dk, dv;
+    float scale;
+    int causal;
+    float softcap;
+};
+
+// Returns false if (dk, dv) has no compiled instance.
+bool prefill_supported(int dk, int dv);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    void* o;
+    const float* sinks;
+    int o_f32;
+    int B, Hq, Hkv, Sq, Sk_max, dk, dv;
+    float scale;
+    int causal;
+    float softcap;
+    // paged mode
+    const int32_t* block_table;
+    int block_size;
+    int max_blocks;
+    const int32_t* seq_lens;
+    // gathered mode
+    const int32_t* row_index;
+    const float* key_pos;
+    const int32_t* q_pos;
+    int n_sel;
+    int64_t row_stride;
+    // split-KV scratch
+    void* workspace;
+};
+
+struct DecodePlan {
+    int split_len;   // keys per split (multiple of the kernel's key tile)
+    int n_split;     // ceil(Sk_max / split_len)
+    int n_rows;      // B * Sq * Hq output rows
+    size_t ws_bytes; // partial O (fp32, dv per row per split) + (max, sum) per row per split
+};
+
+bool decode_supported(int dk, int dv, bool gathered);
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+}  // namespace attn

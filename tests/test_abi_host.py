@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented status before any HIP
+call (so these run without a GPU; no compute call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_flash_attn_amd as attn
+from attention_flash_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.library_path()),
+                                reason="libattn.so not built (run __graft_entry__.build())")
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = binding.load_library()
+    names = declared_functions()
+    assert {"attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), "symbol %s missing from libattn.so" % n
+
+
+def test_abi_version_matches_header():
+    with open(HEADER) as f:
+        ver = int(re.search(r"#define ATTN_ABI_VERSION (\d+)", f.read()).group(1))
+    assert attn.attn_abi_version() == ver
+    assert attn.attn_status_string(0) == "ok"
+    assert attn.attn_status_string(2) == "unsupported configuration"
+
+
+def prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, od=0, lse=None, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, dk=64, dv=64,
+             scale=0.125, causal=0, softcap=0.0, sinks=None, stream=None)
+    a.update(kw)
+    return lib.attn_prefill_fwd(a["q"], a["k"], a["v"], a["o"], a["od"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                a["Sq"], a["Sk"], a["dk"], a["dv"], a["scale"], a["causal"], a["softcap"],
+                                a["sinks"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),
+    (dict(o=None), 1),
+    (dict(B=0), 1),
+    (dict(Sk=0), 1),
+    (dict(Hq=3, Hkv=2), 1),
+    (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1),
+    (dict(softcap=-1.0), 1),
+    (dict(od=7), 1),
+    (dict(q=ctypes.c_void_p(0x10002)), 1),
+    (dict(dk=48, dv=48), 2),
+    (dict(dk=128, dv=64), 2),
+    (dict(dk=576, dv=512), 2),
+])
+def test_prefill_rejects(kw, status):
+    lib = binding.load_library()
+    assert prefill(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def decode(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, od=0, B=2, Hq=8, Hkv=1, Sq=1, Sk_max=100, dk=128, dv=128,
+             scale=0.1, causal=0, softcap=0.0, sinks=None, table=FAKE, bs=64, maxb=2, lens=FAKE,
+             rows=None, kpos=None, qpos=None, n_sel=0, stride=0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.attn_decode_fwd(a["q"], a["kc"], a["vc"], a["o"], a["od"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                               a["Sk_max"], a["dk"], a["dv"], a["scale"], a["causal"], a["softcap"], a["sinks"],
+                               a["table"], a["bs"], a["maxb"], a["lens"], a["rows"], a["kpos"], a["qpos"],
+                               a["n_sel"], a["stride"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),
+    (dict(table=None), 1),                                  # neither mode
+    (dict(rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100), 1),  # both modes
+    (dict(lens=None), 1),
+    (dict(bs=48), 1),
+    (dict(maxb=1), 1),                                      # table too short for Sk_max
+    (dict(ws_bytes=16), 1),
+    (dict(ws=None), 1),
+    (dict(Hq=64, Hkv=1), 2),                                # group of 64 > 32 query columns
+    (dict(dk=100, dv=100), 2),
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, Hkv=2, Hq=8), 1),
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=99, stride=128), 1),
+    (dict(table=None, rows=FAKE, kpos=None, qpos=FAKE, n_sel=100, stride=128), 1),
+])
+def test_decode_rejects(kw, status):
+    lib = binding.load_library()
+    assert decode(lib, **kw) == status
+
+
+def test_workspace_bytes():
+    # 512-key splits: ceil(32768/512) = 64 splits, (dv + 2) floats per row per split
+    n = attn.attn_decode_workspace_bytes(64, 64, 8, 1, 32768, 128, 128)
+    assert n >= 64 * 64 * 64 * 130 * 4
+    assert attn.attn_decode_workspace_bytes(0, 64, 8, 1, 100, 128, 128) == 0
+    assert attn.attn_decode_workspace_bytes(2, 6, 4, 1, 100, 128, 128) == 0

@@ -1,0 +1,95 @@
+"""GPU parity of attn_decode_fwd (paged mode) against the fp64 CPU oracle (through the C ABI)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_flash_attn_amd import binding, synth
+from gpu_util import check_close, dev, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_paged(case, scale, causal, softcap, o_dtype, Sk_max):
+    q = dev_bf16(case["q"])
+    kc, vc = dev_bf16(case["k_cache"]), dev_bf16(case["v_cache"])
+    table = dev(case["block_table"])
+    lens = dev(case["seq_lens"])
+    B, Sq, Hq, dk = q.shape
+    Hkv = kc.shape[1]
+    dv = vc.shape[3]
+    o = torch.empty((B, Sq, Hq, dv), device="cuda", dtype=torch.float32 if o_dtype == "f32" else torch.bfloat16)
+    nbytes = binding.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk_max, dk, dv)
+    ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
+    sinks = dev(case["sinks"]) if case["sinks"] is not None else None
+    binding.attn_decode_fwd(q, kc, vc, o, ws, scale=scale, Sk_max=Sk_max, causal=causal, softcap=softcap,
+                            sinks=sinks, block_table=table, seq_lens=lens)
+    torch.cuda.synchronize()
+    return o
+
+
+def check_paged(B, Hq, Hkv, dk, dv, lo, hi, bs=64, Sq=1, causal=False, softcap=0.0, sinks=False, o_dtype="f32",
+                seed=200, lens=None):
+    print("paged B=%d Hq=%d Hkv=%d dk=%d dv=%d len[%d,%d] bs=%d Sq=%d causal=%d softcap=%g sinks=%d %s" %
+          (B, Hq, Hkv, dk, dv, lo, hi, bs, Sq, causal, softcap, sinks, o_dtype), flush=True)
+    case = synth.paged_case(seed, B, Hq, Hkv, dk, dv, lo, hi, block_size=bs, Sq=Sq, sinks=sinks, lens=lens)
+    scale = 1.0 / math.sqrt(dk)
+    Sk_max = int(hi)
+    o = run_paged(case, scale, causal, softcap, o_dtype, Sk_max)
+    ro, _ = oracle.decode_paged(case["q"], case["k_cache"], case["v_cache"], case["block_table"], case["seq_lens"],
+                                scale, causal=causal, softcap=softcap, sinks=case["sinks"])
+    return check_close(host(o), ro, o_dtype, "paged decode")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 64), (96, 96), (128, 128), (192, 192), (256, 256),
+                                   (192, 128)])
+def test_paged_head_dims(dk, dv):
+    check_paged(3, 8, 2, dk, dv, 1, 1300, o_dtype="f32")
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+def test_paged_block_sizes(bs):
+    check_paged(4, 16, 2, 128, 128, 30, 2100, bs=bs, o_dtype="bf16", seed=201)
+
+
+def test_paged_gqa_ratios_and_features():
+    check_paged(5, 32, 1, 64, 64, 500, 1500, o_dtype="f32", seed=202)                 # 32 query heads, 1 KV head
+    check_paged(3, 4, 4, 128, 128, 1, 700, o_dtype="f32", softcap=3.0, sinks=True, seed=203)
+    check_paged(2, 16, 8, 128, 128, 600, 600, Sq=4, causal=True, o_dtype="f32", seed=204)   # Sq > 1 causal
+    check_paged(2, 8, 1, 128, 128, 0, 5, o_dtype="f32", seed=205, lens=[0, 5])        # empty sequence
+
+
+def test_paged_block_permutation_invariance():
+    case = synth.paged_case(206, 3, 8, 1, 128, 128, 100, 1000)
+    o1 = run_paged(case, 0.09, False, 0.0, "f32", 1000)
+    # move every block to a new physical slot and rewrite the table
+    N = case["k_cache"].shape[0]
+    perm = np.random.default_rng(5).permutation(N)
+    case2 = dict(case)
+    case2["k_cache"] = np.empty_like(case["k_cache"])
+    case2["v_cache"] = np.empty_like(case["v_cache"])
+    case2["k_cache"][perm] = case["k_cache"]
+    case2["v_cache"][perm] = case["v_cache"]
+    t = case["block_table"].copy()
+    nblk = (case["seq_lens"] + 63) // 64
+    for b in range(3):
+        t[b, :nblk[b]] = perm[t[b, :nblk[b]]]
+    case2["block_table"] = t
+    o2 = run_paged(case2, 0.09, False, 0.0, "f32", 1000)
+    assert torch.equal(o1, o2)
+
+
+def test_config4_full_size_sampled():
+    c = synth.CONFIGS["c4_paged_gqa_decode"]
+    print("full-size c4 paged decode", flush=True)
+    case = synth.paged_case(c["seed"], c["B"], c["Hq"], c["Hkv"], c["dk"], c["dv"], c["len_lo"], c["len_hi"],
+                            block_size=c["block_size"])
+    o = run_paged(case, c["scale"], False, 0.0, "bf16", c["len_hi"])
+    batches = [0, 1, int(np.argmax(case["seq_lens"])), int(np.argmin(case["seq_lens"])), 63]
+    ro, _ = oracle.decode_paged(case["q"], case["k_cache"], case["v_cache"], case["block_table"],
+                                case["seq_lens"], c["scale"], batches=batches)
+    err, cos = check_close(host(o)[batches], ro, "bf16", "config 4")
+    print("config 4 sampled: max err %.3g cos %.8f" % (err, cos))
