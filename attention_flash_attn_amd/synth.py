@@ -6,7 +6,10 @@ both the HIP path's tests/benchmark and the CPU oracle consume what it returns.
 Every tensor of bf16 values is returned as uint16 bit patterns, produced from
 fp32 draws by round-to-nearest-even.
 
-Recipe (numpy PCG64, seeded per case):
+Recipe (numpy PCG64, seeded per case): every bf16 tensor is drawn in
+4M-element chunks, chunk i of tensor `tag` from the stream
+SeedSequence([seed, tag, i]) (q: tag 0, k or the row cache: 1, v: 2); sinks
+and all index structure come from one PCG64(seed) stream in the order below.
   * prefill: q, k, v ~ N(0, std^2) (fp32 draw scaled by std, then bf16), then
     sinks ~ N(0, 1) fp32 when requested.
   * paged decode: lengths L_b ~ U{lo..hi} first (they fix the cache size), then
@@ -18,6 +21,9 @@ Recipe (numpy PCG64, seeded per case):
     U{n_sel-1..n_rows-1} and n_sel distinct positions <= q_pos (sorted);
     row_index is the physical row of each position, key_pos its fp32 value.
 """
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -44,25 +50,43 @@ def bf16_bits_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def normal_bf16(rng, shape, std=1.0, chunk=1 << 24):
-    """N(0, std^2) draws in fp32, rounded to bf16 bits; drawn in fixed chunks to bound memory."""
+def normal_bf16(seed, tag, shape, std=1.0, chunk=1 << 22, threads=None):
+    """N(0, std^2) draws in fp32, rounded to bf16 bits.
+
+    Chunk i of the flattened tensor is drawn from its own PCG64 stream seeded
+    by SeedSequence([seed, tag, i]); the result does not depend on how many
+    threads draw the chunks.
+    """
     n = int(np.prod(shape)) if len(shape) else 1
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
+    starts = list(range(0, n, chunk))
+
+    def work(i):
+        s = starts[i]
         e = min(n, s + chunk)
-        x = rng.standard_normal(e - s, dtype=np.float32)
+        r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(tag), i])))
+        x = r.standard_normal(e - s, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
         out[s:e] = to_bf16_bits(x)
+
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    if len(starts) <= 1 or threads <= 1:
+        for i in range(len(starts)):
+            work(i)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(len(starts))))
     return out.reshape(shape)
 
 
 def prefill_case(seed, B, Sq, Sk, Hq, Hkv, dk, dv, std=1.0, sinks=False):
     """Dense prefill inputs: q [B,Sq,Hq,dk], k [B,Sk,Hkv,dk], v [B,Sk,Hkv,dv] bf16 bits; sinks [Hq] fp32 or None."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    q = normal_bf16(rng, (B, Sq, Hq, dk), std)
-    k = normal_bf16(rng, (B, Sk, Hkv, dk), std)
-    v = normal_bf16(rng, (B, Sk, Hkv, dv), std)
+    q = normal_bf16(seed, 0, (B, Sq, Hq, dk), std)
+    k = normal_bf16(seed, 1, (B, Sk, Hkv, dk), std)
+    v = normal_bf16(seed, 2, (B, Sk, Hkv, dv), std)
     s = rng.standard_normal(Hq, dtype=np.float32) if sinks else None
     return {"q": q, "k": k, "v": v, "sinks": s}
 
@@ -83,9 +107,9 @@ def paged_case(seed, B, Hq, Hkv, dk, dv, len_lo, len_hi, block_size=64, max_bloc
     N = int(nblk.sum())
     if max_blocks is None:
         max_blocks = int(max(1, -(-int(len_hi) // block_size)))
-    q = normal_bf16(rng, (B, Sq, Hq, dk), std)
-    kc = normal_bf16(rng, (max(N, 1), Hkv, block_size, dk), std)
-    vc = normal_bf16(rng, (max(N, 1), Hkv, block_size, dv), std)
+    q = normal_bf16(seed, 0, (B, Sq, Hq, dk), std)
+    kc = normal_bf16(seed, 1, (max(N, 1), Hkv, block_size, dk), std)
+    vc = normal_bf16(seed, 2, (max(N, 1), Hkv, block_size, dv), std)
     s = rng.standard_normal(Hq, dtype=np.float32) if sinks else None
     perm = rng.permutation(N).astype(np.int32)
     table = np.zeros((B, max_blocks), dtype=np.int32)
@@ -111,8 +135,8 @@ def gathered_case(seed, T, Hq, dk, dv, n_rows, n_sel, row_dim=None, block_rows=6
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     row_dim = dk if row_dim is None else row_dim
-    kv = normal_bf16(rng, (n_rows, row_dim), std)
-    q = normal_bf16(rng, (T, Hq, dk), std)
+    kv = normal_bf16(seed, 1, (n_rows, row_dim), std)
+    q = normal_bf16(seed, 0, (T, Hq, dk), std)
     s = rng.standard_normal(Hq, dtype=np.float32) if sinks else None
     nb = n_rows // block_rows
     block_perm = rng.permutation(nb).astype(np.int64)

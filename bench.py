@@ -1,0 +1,241 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one causal MHA prefill (B=2, Hq=Hkv=32, Sq=Sk=4096, d=128, bf16 out)
+followed by one paged GQA decode (64 sequences, Hq=64, Hkv=8, d=128, lengths
+U{1024..32768}, 64-token blocks placed by a random block table: split kernel +
+combine). Inputs are seeded synthetic tensors resident in HBM before timing.
+
+The JSON line's `value` is prefill TFLOP/s (algorithmic flops: only the
+visible causal pairs, 4*d flops each), timed with HIP events on the stream the
+kernels run on; the decode half of the metric (algorithmic KV bytes per
+second) is in `decode`. Other workloads (GQA d=256 with and without
+causal+softcap+sinks, single-head d=16) are timed after the step loop and
+reported under `other`. `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the prefill workload.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-other] [--gpus 1]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def prefill_flops(c):
+    """Algorithmic flops: 2*(dk+dv) per visible (query, key) pair."""
+    B, Sq, Sk, Hq = c["B"], c["Sq"], c["Sk"], c["Hq"]
+    if c["causal"]:
+        shift = Sk - Sq
+        pairs = sum(max(0, min(Sk, i + shift + 1)) for i in range(Sq))
+    else:
+        pairs = Sq * Sk
+    return 2.0 * (c["dk"] + c["dv"]) * pairs * B * Hq
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-other", action="store_true", help="skip the extra workloads")
+    ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) pairs in the CPU sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the kernels shard over "
+              "(batch, KV head) with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_flash_attn_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---------------- inputs (seeded, synthetic), resident in HBM
+    c2 = synth.CONFIGS["c2_causal_mha_d128"]
+    log("generating prefill inputs")
+    pc = synth.prefill_case(c2["seed"], c2["B"], c2["Sq"], c2["Sk"], c2["Hq"], c2["Hkv"], c2["dk"], c2["dv"],
+                            std=c2["std"])
+    q2, k2, v2 = to_dev(pc["q"]), to_dev(pc["k"]), to_dev(pc["v"])
+    o2 = torch.empty((c2["B"], c2["Sq"], c2["Hq"], c2["dv"]), device=dev, dtype=torch.bfloat16)
+    del pc
+
+    c4 = synth.CONFIGS["c4_paged_gqa_decode"]
+    log("generating paged decode inputs")
+    dc = synth.paged_case(c4["seed"], c4["B"], c4["Hq"], c4["Hkv"], c4["dk"], c4["dv"], c4["len_lo"],
+                          c4["len_hi"], block_size=c4["block_size"])
+    lens_host = dc["seq_lens"].astype(np.int64)
+    q4 = to_dev(dc["q"])
+    kc4, vc4 = to_dev(dc["k_cache"]), to_dev(dc["v_cache"])
+    table4 = torch.from_numpy(dc["block_table"]).to(dev)
+    lens4 = torch.from_numpy(dc["seq_lens"]).to(dev)
+    del dc
+    o4 = torch.empty((c4["B"], 1, c4["Hq"], c4["dv"]), device=dev, dtype=torch.bfloat16)
+    ws_bytes = binding.attn_decode_workspace_bytes(c4["B"], c4["Hq"], c4["Hkv"], 1, c4["len_hi"], c4["dk"],
+                                                   c4["dv"])
+    ws4 = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+
+    flops2 = prefill_flops(c2)
+    kv_bytes4 = float(lens_host.sum()) * c4["Hkv"] * (c4["dk"] + c4["dv"]) * 2
+    io_bytes4 = (q4.numel() + o4.numel()) * 2 + table4.numel() * 4 + lens4.numel() * 4
+    bytes4 = kv_bytes4 + io_bytes4
+
+    def prefill():
+        binding.attn_prefill_fwd(q2, k2, v2, o2, None, scale=c2["scale"], causal=True)
+
+    def decode():
+        binding.attn_decode_fwd(q4, kc4, vc4, o4, ws4, scale=c4["scale"], Sk_max=c4["len_hi"],
+                                block_table=table4, seq_lens=lens4)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = [ev[i][0].elapsed_time(ev[i][1]) * 1e-3 for i in range(K)]
+    t_dec = [ev[i][1].elapsed_time(ev[i][2]) * 1e-3 for i in range(K)]
+    avg_pre = sum(t_pre) / K
+    avg_dec = sum(t_dec) / K
+    tflops = flops2 / avg_pre / 1e12
+    dec_gbs = bytes4 / avg_dec / 1e9
+    log("prefill c2: %.1f us/launch, %.1f TFLOP/s (%.1f%% of peak)" % (avg_pre * 1e6, tflops,
+                                                                        100 * tflops / PEAK_BF16_TFLOPS))
+    log("decode c4: %.1f us/call, %.1f GB/s (%.1f%% of peak)" % (avg_dec * 1e6, dec_gbs, 100 * dec_gbs / PEAK_HBM_GBS))
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal MHA prefill B=2 Hq=Hkv=32 Sq=Sk=4096 dk=dv=128 bf16 out (value) + paged GQA "
+                        "decode B=64 Hq=64 Hkv=8 d=128 lengths U{1024..32768} 64-token blocks (decode)",
+            "prefill_flops_per_launch": flops2,
+            "decode_kv_bytes_per_call": bytes4,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "prefill_kernel<128,128,64,bf16 out>",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_pre * 1e6, 2),
+        },
+        "decode": {
+            "value": round(dec_gbs, 1),
+            "unit": "GB/s",
+            "us_per_call": round(avg_dec * 1e6, 2),
+            "roofline": {"kernel": "decode_paged_split_kernel<128,128> + decode_combine_kernel", "bound": "hbm",
+                         "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        },
+    }
+
+    # ---------------- other workloads (own timing, after the step loop)
+    if not args.no_other:
+        other = {}
+        for name in ("c3a_gqa_d256", "c3b_gqa_d256_causal_softcap", "c1_single_head_d16"):
+            c = synth.CONFIGS[name]
+            log("generating %s" % name)
+            cc = synth.prefill_case(c["seed"], c["B"], c["Sq"], c["Sk"], c["Hq"], c["Hkv"], c["dk"], c["dv"],
+                                    std=c["std"], sinks=c["sinks"])
+            q, k, v = to_dev(cc["q"]), to_dev(cc["k"]), to_dev(cc["v"])
+            sk = torch.from_numpy(cc["sinks"]).to(dev) if cc["sinks"] is not None else None
+            o = torch.empty((c["B"], c["Sq"], c["Hq"], c["dv"]), device=dev,
+                            dtype=torch.float32 if c["o_dtype"] == "f32" else torch.bfloat16)
+
+            def run(q=q, k=k, v=v, o=o, sk=sk, c=c):
+                binding.attn_prefill_fwd(q, k, v, o, None, scale=c["scale"], causal=c["causal"],
+                                         softcap=c["softcap"], sinks=sk)
+            for _ in range(2):
+                run()
+            reps = 10
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / reps
+            f = prefill_flops(c)
+            other[name] = {"us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 2),
+                           "frac_bf16_peak": round(f / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            log("%s: %.1f us, %.1f TFLOP/s" % (name, t * 1e6, f / t / 1e12))
+            del q, k, v, o, cc
+        result["other"] = other
+
+    # ---------------- CPU baseline: the oracle on a bounded sample of the prefill workload
+    if not args.no_cpu:
+        import oracle
+        log("CPU oracle baseline")
+        pc = synth.prefill_case(c2["seed"], c2["B"], c2["Sq"], c2["Sk"], c2["Hq"], c2["Hkv"], c2["dk"], c2["dv"],
+                                std=c2["std"])
+        pairs = [(b, h) for b in range(c2["B"]) for h in range(c2["Hq"])][:args.cpu_heads]
+        t0 = time.perf_counter()
+        for b, h in pairs:
+            oracle.prefill(pc["q"], pc["k"], pc["v"], c2["scale"], causal=True, heads=[h], batches=[b])
+        tc = time.perf_counter() - t0
+        try:  # BLAS threads the oracle's matrix products ran on
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        f = prefill_flops(c2) / (c2["B"] * c2["Hq"]) * len(pairs)
+        result["cpu_baseline"] = {"value": round(f / tc / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+                                  "kind": "oracle",
+                                  "sample": "%d of the 64 (batch, head) pairs of the causal MHA prefill "
+                                            "(4096 x 4096, d=128), fp64 numpy, %.1f s" % (len(pairs), tc)}
+        log("oracle: %.1f s for %d heads -> %.4f TFLOP/s" % (tc, len(pairs), f / tc / 1e12))
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
