@@ -53,6 +53,43 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// v_dot2_f32_bf16: acc + lo(w) + hi(w) for a packed bf16 pair (sum of two rounded probabilities).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane: lane i writes lds_base + 16 * i
+// (lds_base must be wave-uniform). Inactive lanes write nothing.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (ATTN_LDS void*)(reinterpret_cast<uintptr_t>(lds_base)), 16, 0, 0);
+}
+
+// Buffer resource (V#) over [base, base + bytes): offsets >= bytes are out of range.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_buffer(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = (int32_t)(uint32_t)a;
+    r[1] = (int32_t)(uint32_t)(a >> 32);  // stride 0
+    r[2] = (int32_t)bytes;                // num_records (bytes)
+    r[3] = 0x00020000;                    // gfx9-family data format word
+    return r;
+}
+constexpr uint32_t kOobOffset = 0x80000000u;  // an offset that is always out of range
+
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, ATTN_LDS uint32_t* lds, int size, int voffset,
+                                                           int soffset, int offset,
+                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Buffer -> LDS copy of 16 bytes per lane (lane i writes lds_base + 16 * i); an out-of-range
+// offset must not be relied on to write anything.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 rsrc, uint32_t voffset, void* lds_base) {
+    llvm_amdgcn_raw_buffer_load_lds(rsrc, (ATTN_LDS uint32_t*)(reinterpret_cast<uintptr_t>(lds_base)), 16,
+                                    (int)voffset, 0, 0, 0);
+}
+// Wait until this wave's outstanding vector-memory loads (incl. direct-to-LDS) completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Transposing LDS read: 4 bf16 (one column of a 4 x 16 block per lane, see above).
 __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(

@@ -1,4 +1,4 @@
-// Fused prefill attention for gfx950: one workgroup per (128-query tile, query head, batch).
+// Fused prefill attention for gfx950: one workgroup per (query tile, query head, batch).
 //
 // Follows the tensor kernel of the "ggml-metal: FA tensor path: gate to the
 // (256, 256) shape" page in what it computes (raw QK^T product, scale, softcap,
@@ -7,26 +7,35 @@
 // written as 0, GQA head map h / (Hq / Hkv)) but not in how: the design here is
 // built around CDNA4's 32x32x16 bf16 MFMA and wave64.
 //
-//  * Each of the 4 waves owns 32 query rows. The score tile is computed
-//    transposed, S^T = K Q^T, so every lane holds the scores of ONE query
-//    (column lane%32) for 16 keys per 32-key block: the row max is an
-//    in-register reduction plus one permlane32 swap, the row sum needs no
-//    cross-lane step until the end, and the O rescale factor is lane-local.
-//    (The same idea as the key-major score layout on the "MLA Decode Attention
-//    Kernel API Reference" page, Notes.)
+//  * Each wave owns 32 query rows. The score tile is computed transposed,
+//    S^T = K Q^T, so every lane holds the scores of ONE query (column
+//    lane%32) for 16 keys per 32-key block: the row max is an in-register
+//    reduction plus one permlane32 swap, the row sum needs no cross-lane step
+//    until the end, and the O rescale factor is lane-local. (The key-major
+//    score layout of the "MLA Decode Attention Kernel API Reference" page,
+//    Notes, is the same idea.)
 //  * O is accumulated transposed too, O^T += V^T P^T: the S^T accumulator
 //    registers of a lane are exactly its P^T operand for the PV MFMA (after a
 //    bf16 pack), so P never leaves registers. The key order inside a 16-key
 //    step is permuted to match; the V^T operand is read from LDS with
 //    ds_read_b64_tr_b16 in that same key order.
-//  * K/V tiles of BN keys are staged in LDS with coalesced 16-byte loads,
-//    double-buffered (next tile's global loads are in flight during the
-//    current tile's math), XOR-swizzled by 16-byte chunk.
-//  * Scores are kept in log2 units (scale * log2 e folded into one multiply)
-//    so every exponential is one v_exp_f32.
-//  * Causal: tiles past the workgroup's last visible key are never loaded,
-//    a wave skips tiles wholly above its diagonal, and only tiles crossing the
-//    diagonal or the end of the keys evaluate the mask.
+//  * K/V tiles of BN keys go HBM -> LDS directly (global_load_lds, 16 bytes
+//    per lane, 1 KB per wave instruction), double-buffered: tile t+1 is in
+//    flight while tile t is computed; one barrier per tile. Rows are
+//    XOR-swizzled by 16-byte chunk so both read patterns are conflict-free.
+//  * Scores stay in log2 units (scale * log2 e folded into one FMA with the
+//    max) so every exponential is one v_exp_f32. The running max moves only
+//    when a tile's max exceeds it by more than 2^8 (O and the sum use the same
+//    reference, so the result is unchanged; probabilities stay <= 256), which
+//    lets the O rescale be skipped for the whole wave on most tiles.
+//  * Row sums add the bf16-rounded probabilities two at a time (v_dot2), so O
+//    is an exact convex combination of V rows up to fp32 accumulation.
+//  * Causal: tiles past the workgroup's last visible key are never loaded, a
+//    wave skips tiles wholly above its diagonal, and only tiles crossing the
+//    diagonal or the end of the keys evaluate the mask. Workgroups are
+//    ordered heaviest query tile first, with heads spread over the 8 XCDs.
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
@@ -44,16 +53,16 @@ struct PrefillParams {
     float c_score;  // scale * log2 e                (softcap off)
     float c_tanh;   // 2 * scale / softcap * log2 e  (softcap on: exponent of e^{2y})
     float c_cap;    // softcap * log2 e
-    int causal;
-    int softcap_on;
+    int xcd_remap;  // B * Hq is a multiple of 8
 };
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
-template <int DK, int DV, int BN, bool OF32>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
+template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool OF32>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
+void prefill_kernel(PrefillParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int BM = NW * 32;             // query rows per workgroup
     constexpr int DVP = DV < 32 ? 32 : DV;  // V rows padded to a whole 32-row block of O^T
     constexpr int NCK = DK / 8;             // 16-byte chunks per K row
     constexpr int NCV = DVP / 8;            // 16-byte chunks per (padded) V row in LDS
@@ -64,11 +73,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     constexpr int K_BYTES = BN * DK * 2;
     constexpr int V_BYTES = BN * DVP * 2;
     constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int LK = (BN * NCK + kThreads - 1) / kThreads;
-    constexpr int LV = (BN * NCVG + kThreads - 1) / kThreads;
+    constexpr int KSEG = K_BYTES / 1024, VSEG = V_BYTES / 1024;  // 1 KB load segments per tile
     static_assert(DK % 16 == 0 && DV % 16 == 0 && BN % 32 == 0, "tile shape");
+    static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "tile must split into 1 KB segments");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -76,24 +85,73 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int half = lane >> 5;
     const int col = lane & 31;
 
+    // workgroup -> (query tile, head, batch): heaviest tiles first; with
+    // xcd_remap, XCD x (= blockIdx % 8) works on heads x, x+8, ...
     const int HB = p.Hq * p.B;
-    const int bid = blockIdx.x;
-    const int qt = p.nqt - 1 - bid / HB;  // heaviest (latest) query tiles first
-    const int hb = bid % HB;
+    int qt, hb;
+    if (p.xcd_remap) {
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3, per = HB >> 3;
+        qt = p.nqt - 1 - j / per;
+        hb = x + 8 * (j % per);
+    } else {
+        qt = p.nqt - 1 - blockIdx.x / HB;
+        hb = blockIdx.x % HB;
+    }
     const int h = hb % p.Hq;
     const int b = hb / p.Hq;
     const int g = h / p.group;
-    const int q0 = qt * kBM + wave * 32;
+    const int q0 = qt * BM + wave * 32;
     const int qi = q0 + col;
     const int shift = p.Sk - p.Sq;
 
-    if constexpr (DVP != DV) {
-        // padding columns of V must read as zero; tile loads never write them
-        for (int i = tid; i < 2 * STAGE / 16; i += kThreads) {
-            const int s = i / (STAGE / 16), off = (i % (STAGE / 16)) * 16;
-            if (off >= K_BYTES) *(u32x4*)(smem + s * STAGE + off) = u32x4{0, 0, 0, 0};
-        }
+    int kv_end = p.Sk;
+    if (CAUSAL) kv_end = min(p.Sk, qt * BM + BM + shift);
+    const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+    // Rows at or past Sk (and the V padding columns) fall outside the buffer
+    // ranges below and are not loaded: start both stages at zero so those LDS
+    // rows always hold finite values (zero, or an earlier tile's data); their
+    // scores are masked and their probabilities are exactly 0.
+    if ((DVP != DV) || (p.Sk % BN) != 0) {
+        for (int i = tid; i < 2 * STAGE / 16; i += NT) *(u32x4*)(smem + i * 16) = u32x4{0, 0, 0, 0};
+        __syncthreads();
     }
+
+    // K and V of this (batch, KV head) as buffers
+    const size_t kstride = (size_t)p.Hkv * DK, vstride = (size_t)p.Hkv * DV;
+    const i32x4 krsrc = make_buffer(p.k + (size_t)b * p.Sk * kstride + (size_t)g * DK,
+                                    (uint32_t)(((size_t)(p.Sk - 1) * kstride + DK) * 2));
+    const i32x4 vrsrc = make_buffer(p.v + (size_t)b * p.Sk * vstride + (size_t)g * DV,
+                                    (uint32_t)(((size_t)(p.Sk - 1) * vstride + DV) * 2));
+
+    // issue the direct-to-LDS loads of tile t into stage st (each wave: every NW-th 1 KB segment)
+    auto issue = [&](int t, int st) {
+        char* sb = smem + st * STAGE;
+        const int key0 = t * BN;
+#pragma unroll
+        for (int i = 0; i < (KSEG + NW - 1) / NW; ++i) {
+            const int s = wave + i * NW;
+            if (s < KSEG) {
+                const int off = s * 1024 + lane * 16;
+                const int r = off / (DK * 2);
+                const int c = ((off % (DK * 2)) >> 4) ^ swz<NCK>(r);
+                buffer_load_lds16(krsrc, (uint32_t)((key0 + r) * kstride * 2 + c * 16), sb + s * 1024);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < (VSEG + NW - 1) / NW; ++i) {
+            const int s = wave + i * NW;
+            if (s < VSEG) {
+                const int off = s * 1024 + lane * 16;
+                const int r = off / (DVP * 2);
+                const int c = ((off % (DVP * 2)) >> 4) ^ swz<NCV>(r);
+                const uint32_t vo = c < NCVG ? (uint32_t)((key0 + r) * vstride * 2 + c * 16) : kOobOffset;
+                buffer_load_lds16(vrsrc, vo, sb + K_BYTES + s * 1024);
+            }
+        }
+    };
+
+    if (ntiles > 0) issue(0, 0);
 
     // this lane's Q fragments: row qi, chunks 2*kk + half
     bf16x8 qf[KK];
@@ -107,161 +165,130 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         }
     }
 
-    int kv_end = p.Sk;
-    if (p.causal) kv_end = min(p.Sk, qt * kBM + kBM + shift);
-    const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-
-    const uint16_t* kbase = p.k + (size_t)b * p.Sk * p.Hkv * DK + (size_t)g * DK;
-    const uint16_t* vbase = p.v + (size_t)b * p.Sk * p.Hkv * DV + (size_t)g * DV;
-    const size_t kstride = (size_t)p.Hkv * DK, vstride = (size_t)p.Hkv * DV;
-
-    u32x4 kreg[LK], vreg[LV];
-    auto gload = [&](int t) {
-#pragma unroll
-        for (int i = 0; i < LK; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx / NCK, c = idx % NCK;
-            const int key = t * BN + r;
-            u32x4 w = {0, 0, 0, 0};
-            if (idx < BN * NCK && key < p.Sk) w = *(const u32x4*)(kbase + key * kstride + c * 8);
-            kreg[i] = w;
-        }
-#pragma unroll
-        for (int i = 0; i < LV; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx / NCVG, c = idx % NCVG;
-            const int key = t * BN + r;
-            u32x4 w = {0, 0, 0, 0};
-            if (idx < BN * NCVG && key < p.Sk) w = *(const u32x4*)(vbase + key * vstride + c * 8);
-            vreg[i] = w;
-        }
-    };
-    auto lstore = [&](int s) {
-        char* kt = smem + s * STAGE;
-        char* vt = kt + K_BYTES;
-#pragma unroll
-        for (int i = 0; i < LK; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx / NCK, c = idx % NCK;
-            if (idx < BN * NCK) *(u32x4*)(kt + r * (DK * 2) + ((c ^ swz<NCK>(r)) * 16)) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < LV; ++i) {
-            const int idx = tid + i * kThreads;
-            const int r = idx / NCVG, c = idx % NCVG;
-            if (idx < BN * NCVG) *(u32x4*)(vt + r * (DVP * 2) + ((c ^ swz<NCV>(r)) * 16)) = vreg[i];
-        }
-    };
-
     f32x16 oacc[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
-    float m_run = -INFINITY;  // running max of this lane's query (log2 units), same in both halves
+    float m_run = -INFINITY;  // reference max of this lane's query (log2 units), same in both halves
     float l_run = 0.f;        // this lane's share of the running sum (its half of each key block)
+    const int lim = CAUSAL ? min(p.Sk - 1, qi + shift) : p.Sk - 1;  // last visible key of this row
+    const int trow = (lane & 15) >> 2;                             // row within a 4-row tr block
+    const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;      // column within a 32-col block
 
-    if (ntiles > 0) {
-        gload(0);
-        lstore(0);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int s = t & 1;
-        if (t + 1 < ntiles) gload(t + 1);
-        const int key0 = t * BN;
-        const bool skip = p.causal && (key0 > q0 + 31 + shift);  // wave-uniform
-        if (!skip) {
-            const char* kt = smem + s * STAGE;
-            const char* vt = kt + K_BYTES;
-
-            // S^T = K Q^T for this tile
-            f32x16 sacc[KB];
+    auto tile = [&](const char* kt, const char* vt, int key0, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        // S^T = K Q^T; K fragments are read from LDS PF steps ahead of their MFMA
+        constexpr int NQK = KB * KK;
+        constexpr int PFK = NQK < 4 ? NQK : 4;
+        auto kload = [&](int idx) -> bf16x8 {
+            const int kb = idx / KK, kk = idx % KK;
+            const int r = kb * 32 + col;
+            const int c = 2 * kk + half;
+            return *(const bf16x8*)(kt + r * (DK * 2) + ((c ^ swz<NCK>(r)) * 16));
+        };
+        f32x16 sacc[KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                sacc[kb] = f32x16{};
-                const int r = kb * 32 + col;
-                const char* krow = kt + r * (DK * 2);
+        for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x16{};
+        bf16x8 kring[PFK];
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const int c = 2 * kk + half;
-                    const bf16x8 a = *(const bf16x8*)(krow + ((c ^ swz<NCK>(r)) * 16));
-                    sacc[kb] = mfma32x32x16(a, qf[kk], sacc[kb]);
+        for (int i = 0; i < PFK; ++i) kring[i] = kload(i);
+#pragma unroll
+        for (int idx = 0; idx < NQK; ++idx) {
+            const bf16x8 a = kring[idx % PFK];
+            if (idx + PFK < NQK) kring[idx % PFK] = kload(idx + PFK);
+            sacc[idx / KK] = mfma32x32x16(a, qf[idx % KK], sacc[idx / KK]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // scores in log2 units (softcap) or raw (scaled inside the exponent), mask, tile max
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = sacc[kb][i];
+                if constexpr (SOFTCAP) {
+                    // cap * tanh(y), y = scale*x/cap, tanh(y) = 1 - 2 / (e^{2y} + 1), in log2 units
+                    const float e = exp2_fast(x * p.c_tanh);
+                    x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
                 }
-            }
-
-            // score transform (scale, softcap) into log2 units, mask, tile max
-            const bool need_mask = (key0 + BN > p.Sk) || (p.causal && key0 + BN - 1 > q0 + shift);
-            const int lim = p.causal ? min(p.Sk - 1, qi + shift) : p.Sk - 1;
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float x = sacc[kb][i];
-                    if (p.softcap_on) {
-                        // cap * tanh(y), y = scale*x/cap; tanh(y) = 1 - 2 / (e^{2y} + 1)
-                        const float e = exp2_fast(x * p.c_tanh);
-                        x = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * p.c_cap;
-                    } else {
-                        x *= p.c_score;
-                    }
-                    if (need_mask) {
-                        const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-                        if (key > lim) x = -INFINITY;
-                    }
-                    sacc[kb][i] = x;
-                    tmax = fmaxf(tmax, x);
+                if constexpr (MASK) {
+                    const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+                    if (key > lim) x = -INFINITY;
                 }
-            }
-            tmax = halfwave_max(tmax);
-            const float m_new = fmaxf(m_run, tmax);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = exp2_fast(m_run - m_use);
-            m_run = m_new;
-
-            // P = 2^(x - m) rounded to bf16 and packed as the PV operand; the
-            // running sum uses the rounded values so O stays a convex combination
-            uint32_t pk[KB][8];
-            float psum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t w = pack_bf16x2(exp2_fast(sacc[kb][2 * j] - m_use),
-                                                   exp2_fast(sacc[kb][2 * j + 1] - m_use));
-                    pk[kb][j] = w;
-                    psum += bf16lo_to_f32(w) + bf16hi_to_f32(w);
-                }
-            }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
-
-            // O^T += V^T P^T, 16 keys per MFMA
-            const int trow = (lane & 15) >> 2;                       // row within the 4-row block
-            const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;  // column within the 32-col block
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
-                    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-                    const int ra = kb * 32 + 16 * jj + half * 4 + trow;
-                    const int rb = ra + 8;
-#pragma unroll
-                    for (int d = 0; d < DB; ++d) {
-                        const int dc = d * 32 + tcol;
-                        const int ch = dc >> 3, within = (dc & 7) * 2;
-                        const bf16x4 va = lds_read_tr16(vt + ra * (DVP * 2) + ((ch ^ swz<NCV>(ra)) * 16) + within);
-                        const bf16x4 vb = lds_read_tr16(vt + rb * (DVP * 2) + ((ch ^ swz<NCV>(rb)) * 16) + within);
-                        const bf16x8 a = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                        oacc[d] = mfma32x32x16(a, pb, oacc[d]);
-                    }
-                }
+                sacc[kb][i] = x;
+                mx = fmaxf(mx, x);
             }
         }
-        if (t + 1 < ntiles) lstore(s ^ 1);
-        __syncthreads();
+        mx = halfwave_max(mx);
+        const float cs = SOFTCAP ? 1.f : p.c_score;
+        const float m_tile = SOFTCAP ? mx : mx * cs;
+        // lazy reference update: only when the tile max exceeds the reference by > 2^tau
+        const bool upd = m_tile > m_run + kTau;
+        if (__builtin_amdgcn_ballot_w64(upd)) {
+            // lanes that keep their reference (possibly still -inf) scale by exactly 1
+            const float alpha = upd ? exp2_fast(m_run - m_tile) : 1.f;  // 0 when m_run = -inf
+            m_run = upd ? m_tile : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        const float nm = -m_use;
+        // P = 2^(s - m) rounded to bf16, packed as the PV operand; sum of the rounded values
+        uint32_t pk[KB][8];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][2 * j], cs, nm));
+                const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][2 * j + 1], cs, nm));
+                pk[kb][j] = pack_bf16x2(p0, p1);
+                l_run = add_bf16x2(pk[kb][j], l_run);
+            }
+        }
+        // O^T += V^T P^T, 16 keys per MFMA; V^T fragments read PF steps ahead
+        constexpr int NPV = KB * 2 * DB;
+        constexpr int PFV = NPV < 4 ? NPV : 4;
+        auto vload = [&](int idx) -> bf16x8 {
+            const int d = idx % DB, jj = (idx / DB) % 2, kb = idx / (2 * DB);
+            const int ra = kb * 32 + 16 * jj + half * 4 + trow;
+            const int rb = ra + 8;
+            const int dc = d * 32 + tcol;
+            const int ch = dc >> 3, within = (dc & 7) * 2;
+            const bf16x4 va = lds_read_tr16(vt + ra * (DVP * 2) + ((ch ^ swz<NCV>(ra)) * 16) + within);
+            const bf16x4 vb = lds_read_tr16(vt + rb * (DVP * 2) + ((ch ^ swz<NCV>(rb)) * 16) + within);
+            return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 vring[PFV];
+#pragma unroll
+        for (int i = 0; i < PFV; ++i) vring[i] = vload(i);
+#pragma unroll
+        for (int idx = 0; idx < NPV; ++idx) {
+            const int d = idx % DB, jj = (idx / DB) % 2, kb = idx / (2 * DB);
+            const bf16x8 a = vring[idx % PFV];
+            if (idx + PFV < NPV) vring[idx % PFV] = vload(idx + PFV);
+            const u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
+            oacc[d] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, pw), oacc[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+#pragma clang loop unroll(disable)
+    for (int t = 0; t < ntiles; ++t) {
+        wait_vmem();       // this wave's loads of tile t have landed in LDS
+        __syncthreads();   // ... and every other wave's; stage (t+1)&1 is free again
+        if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int key0 = t * BN;
+        const char* kt = smem + (t & 1) * STAGE;
+        const char* vt = kt + K_BYTES;
+        const bool skip = CAUSAL && (key0 > q0 + 31 + shift);  // wave-uniform
+        if (!skip) {
+            const bool need_mask = (key0 + BN > p.Sk) || (CAUSAL && key0 + BN - 1 > q0 + shift);
+            if (need_mask)
+                tile(kt, vt, key0, std::true_type{});
+            else
+                tile(kt, vt, key0, std::false_type{});
+        }
     }
 
     // epilogue: sinks, normalisation, store
@@ -297,14 +324,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     }
 }
 
-template <int DK, int DV, int BN>
-hipError_t launch_inst(const PrefillParams& p, bool of32, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.nqt * p.Hq * p.B)), block(kThreads);
+template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP>
+hipError_t launch_variant(PrefillParams p, bool of32, hipStream_t stream) {
+    constexpr int BM = NW * 32;
+    p.nqt = (p.Sq + BM - 1) / BM;
+    const dim3 grid((unsigned)(p.nqt * p.Hq * p.B)), block(NW * 64);
     if (of32)
-        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, true>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, false>), grid, block, 0, stream, p);
     return hipGetLastError();
+}
+
+template <int DK, int DV, int BN, int NW, int OCC>
+hipError_t launch_inst(const PrefillParams& p, bool causal, bool softcap, bool of32, hipStream_t stream) {
+    if (causal) {
+        return softcap ? launch_variant<DK, DV, BN, NW, OCC, true, true>(p, of32, stream)
+                       : launch_variant<DK, DV, BN, NW, OCC, true, false>(p, of32, stream);
+    }
+    return softcap ? launch_variant<DK, DV, BN, NW, OCC, false, true>(p, of32, stream)
+                   : launch_variant<DK, DV, BN, NW, OCC, false, false>(p, of32, stream);
 }
 
 }  // namespace
@@ -333,22 +372,22 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     p.Sq = a.Sq;
     p.Sk = a.Sk;
     p.group = a.Hq / a.Hkv;
-    p.nqt = (a.Sq + kBM - 1) / kBM;
+    p.nqt = 0;
     p.c_score = a.scale * kLog2e;
-    p.softcap_on = a.softcap != 0.f;
-    p.c_tanh = p.softcap_on ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
+    const bool softcap = a.softcap != 0.f;
+    p.c_tanh = softcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
     p.c_cap = a.softcap * kLog2e;
-    p.causal = a.causal;
-    const bool of32 = a.o_f32 != 0;
+    p.xcd_remap = ((a.B * a.Hq) % 8) == 0;
+    const bool of32 = a.o_f32 != 0, causal = a.causal != 0;
     switch (a.dk * 1000 + a.dv) {
-        case 16016: return launch_inst<16, 16, 64>(p, of32, stream);
-        case 32032: return launch_inst<32, 32, 64>(p, of32, stream);
-        case 64064: return launch_inst<64, 64, 64>(p, of32, stream);
-        case 96096: return launch_inst<96, 96, 64>(p, of32, stream);
-        case 128128: return launch_inst<128, 128, 64>(p, of32, stream);
-        case 192192: return launch_inst<192, 192, 64>(p, of32, stream);
-        case 256256: return launch_inst<256, 256, 64>(p, of32, stream);
-        case 192128: return launch_inst<192, 128, 64>(p, of32, stream);
+        case 16016: return launch_inst<16, 16, 64, 4, 2>(p, causal, softcap, of32, stream);
+        case 32032: return launch_inst<32, 32, 64, 4, 2>(p, causal, softcap, of32, stream);
+        case 64064: return launch_inst<64, 64, 64, 4, 2>(p, causal, softcap, of32, stream);
+        case 96096: return launch_inst<96, 96, 64, 4, 2>(p, causal, softcap, of32, stream);
+        case 128128: return launch_inst<128, 128, 64, 4, 2>(p, causal, softcap, of32, stream);
+        case 192192: return launch_inst<192, 192, 64, 4, 1>(p, causal, softcap, of32, stream);
+        case 256256: return launch_inst<256, 256, 64, 4, 1>(p, causal, softcap, of32, stream);
+        case 192128: return launch_inst<192, 128, 64, 4, 1>(p, causal, softcap, of32, stream);
         default: return hipErrorInvalidValue;
     }
 }
