@@ -58,6 +58,14 @@ struct PrefillParams {
 
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
+// Tile configurations (keys per tile, waves per workgroup, target waves per SIMD)
+#ifndef ATTN_D128_CFG
+#define ATTN_D128_CFG 64, 4, 2
+#endif
+#ifndef ATTN_D256_CFG
+#define ATTN_D256_CFG 64, 4, 1
+#endif
+
 template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillParams p) {
@@ -199,24 +207,32 @@ void prefill_kernel(PrefillParams p) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // scores in log2 units (softcap) or raw (scaled inside the exponent), mask, tile max
+        if constexpr (SOFTCAP) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    // cap * tanh(y), y = scale*x/cap, tanh(y) = 1 - 2 / (e^{2y} + 1), in log2 units
+                    const float e = exp2_fast(sacc[kb][i] * p.c_tanh);
+                    sacc[kb][i] = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
+                }
+            }
+        }
+        if constexpr (MASK) {  // diagonal and last tiles only
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+                    if (key > lim) sacc[kb][i] = -INFINITY;
+                }
+            }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = sacc[kb][i];
-                if constexpr (SOFTCAP) {
-                    // cap * tanh(y), y = scale*x/cap, tanh(y) = 1 - 2 / (e^{2y} + 1), in log2 units
-                    const float e = exp2_fast(x * p.c_tanh);
-                    x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
-                }
-                if constexpr (MASK) {
-                    const int key = key0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-                    if (key > lim) x = -INFINITY;
-                }
-                sacc[kb][i] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
         }
         mx = halfwave_max(mx);
         const float cs = SOFTCAP ? 1.f : p.c_score;
@@ -272,23 +288,30 @@ void prefill_kernel(PrefillParams p) {
         }
     };
 
-#pragma clang loop unroll(disable)
-    for (int t = 0; t < ntiles; ++t) {
+    // Tiles [0, t_full) are visible to every row of the workgroup and run
+    // without a mask; the rest (diagonal and ragged last tile) run masked.
+    // Two separate loops keep each loop body one straight-line tile.
+    int t_full = p.Sk / BN;
+    if (CAUSAL) t_full = min(t_full, max(0, (qt * BM + shift + 1) / BN));
+    t_full = min(t_full, ntiles);
+    auto step = [&](int t) {
         wait_vmem();       // this wave's loads of tile t have landed in LDS
         __syncthreads();   // ... and every other wave's; stage (t+1)&1 is free again
         if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
-        const int key0 = t * BN;
+    };
+#pragma clang loop unroll(disable)
+    for (int t = 0; t < t_full; ++t) {
+        step(t);
         const char* kt = smem + (t & 1) * STAGE;
-        const char* vt = kt + K_BYTES;
-        const bool skip = CAUSAL && (key0 > q0 + 31 + shift);  // wave-uniform
-        if (!skip) {
-            const bool need_mask = (key0 + BN > p.Sk) || (CAUSAL && key0 + BN - 1 > q0 + shift);
-            if (need_mask)
-                tile(kt, vt, key0, std::true_type{});
-            else
-                tile(kt, vt, key0, std::false_type{});
-        }
+        tile(kt, kt + K_BYTES, t * BN, std::false_type{});
+    }
+#pragma clang loop unroll(disable)
+    for (int t = t_full; t < ntiles; ++t) {
+        step(t);
+        const char* kt = smem + (t & 1) * STAGE;
+        const bool skip = CAUSAL && (t * BN > q0 + 31 + shift);  // wave-uniform
+        if (!skip) tile(kt, kt + K_BYTES, t * BN, std::true_type{});
     }
 
     // epilogue: sinks, normalisation, store
@@ -384,10 +407,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         case 32032: return launch_inst<32, 32, 64, 4, 2>(p, causal, softcap, of32, stream);
         case 64064: return launch_inst<64, 64, 64, 4, 2>(p, causal, softcap, of32, stream);
         case 96096: return launch_inst<96, 96, 64, 4, 2>(p, causal, softcap, of32, stream);
-        case 128128: return launch_inst<128, 128, 64, 4, 2>(p, causal, softcap, of32, stream);
-        case 192192: return launch_inst<192, 192, 64, 4, 1>(p, causal, softcap, of32, stream);
-        case 256256: return launch_inst<256, 256, 64, 4, 1>(p, causal, softcap, of32, stream);
-        case 192128: return launch_inst<192, 128, 64, 4, 1>(p, causal, softcap, of32, stream);
+        case 128128: return launch_inst<128, 128, ATTN_D128_CFG>(p, causal, softcap, of32, stream);
+        case 192192: return launch_inst<192, 192, 32, 4, 2>(p, causal, softcap, of32, stream);
+        case 256256: return launch_inst<256, 256, ATTN_D256_CFG>(p, causal, softcap, of32, stream);
+        case 192128: return launch_inst<192, 128, 32, 4, 2>(p, causal, softcap, of32, stream);
         default: return hipErrorInvalidValue;
     }
 }
