@@ -6,8 +6,12 @@
 //     lane l holds   D[row (i/4)*8 + (l/32)*4 + i%4][col l%32] in accumulator i = 0..15
 //   ds_read_b64_tr_b16 (per 16-lane group): lane 4r + c points at 4 bf16 of row r,
 //     columns 4c..4c+3 of a 4 x 16 block; lane i receives column i, rows 0..3.
+//   v_mfma_f32_16x16x32_bf16  A[16 x 32], B[32 x 16], D[16 x 16]
+//     lane l supplies A[row l%16][k (l/16)*8 + e] and B[k (l/16)*8 + e][col l%16], e = 0..7
+//     lane l holds   D[row (l/16)*4 + i][col l%16] in accumulator i = 0..3
 //   v_permlane32_swap(x, x) returns {x[l%32], x[l%32 + 32]} in some order on
-//     every lane, so max/sum of the pair combines the two half-waves.
+//     every lane, so max/sum of the pair combines the two half-waves;
+//     v_permlane16_swap(x, x) does the same for lanes l and l^16.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,6 +47,20 @@ __device__ __forceinline__ float halfwave_max(float x) {
 __device__ __forceinline__ float halfwave_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max / sum across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float quarterwave_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return halfwave_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quarterwave_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return halfwave_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Round two floats to bf16 (nearest even) and pack them, low half first.

@@ -23,8 +23,6 @@
 namespace attn {
 namespace {
 
-constexpr int kSplitLen = 512;  // keys per split (16 steps of 32 keys)
-
 struct SplitParams {
     const uint16_t* __restrict__ q;
     const uint16_t* __restrict__ kc;
@@ -34,175 +32,235 @@ struct SplitParams {
     const int32_t* __restrict__ block_table;
     const int32_t* __restrict__ seq_lens;
     int B, Hq, Hkv, Sq, group, nq, bs_log2, max_blocks;
-    int n_split;
+    int n_split, split_len;
     float c_score, c_tanh, c_cap;
     int causal, softcap_on;
 };
 
-template <int DK, int DV>
-__global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
-    constexpr int DVP = DV < 32 ? 32 : DV;
-    constexpr int NCK = DK / 8;
-    constexpr int NCV = DVP / 8;
-    constexpr int NCVG = DV / 8;
-    constexpr int KK = DK / 16;
-    constexpr int DB = DVP / 32;
-    constexpr int LV = (32 * NCVG + 63) / 64;
-    (void)NCK;
-    __shared__ __attribute__((aligned(16))) char vl[32 * DVP * 2];
+constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units), as in the prefill kernel
 
-    const int lane = threadIdx.x, half = lane >> 5, col = lane & 31;
+// One wavefront per (split, KV head, sequence). 32 keys per step on
+// 16x16x32 MFMA: S^T[16 keys x 16 query columns] blocks, so a lane holds 4
+// keys of one query column per block; up to CB blocks of 16 query columns.
+// K fragments go HBM -> registers one step ahead; V rows go HBM -> LDS (one
+// 1 KB direct load per instruction) one step ahead into a per-wave double
+// buffer, for the transposing read of the V^T operand.
+template <int DK, int DV, int CB>
+__global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
+    constexpr int DKP = DK < 32 ? 32 : DK;  // QK k-steps of 32 (zero-padded)
+    constexpr int KQ = DKP / 32;
+    constexpr int DBV = DV / 16;            // 16-row blocks of O^T
+    constexpr int NCV = DV / 8;             // 16-byte chunks per V row
+    constexpr int VROW = DV * 2;            // bytes per V row
+    constexpr int STAGE = 32 * VROW;        // one step of V
+    constexpr int VSEG = STAGE / 1024;      // 1 KB direct-load instructions per step
+    static_assert(STAGE % 1024 == 0, "V step must split into 1 KB segments");
+    __shared__ __attribute__((aligned(1024))) char vl[2 * STAGE];
+
+    const int lane = threadIdx.x, grp = lane >> 4, c16 = lane & 15;
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int L = p.seq_lens[b];
-    const int start = split * kSplitLen;
+    const int start = split * p.split_len;
     if (start >= L) return;  // the combine pass only reads splits that start below L
-    const int end = min(L, start + kSplitLen);
+    const int end = min(L, start + p.split_len);
     const int bs = 1 << p.bs_log2;
+    const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
 
-    if constexpr (DVP != DV) {
-        for (int i = lane; i < 32 * DVP * 2 / 16; i += 64) *(u32x4*)(vl + i * 16) = u32x4{0, 0, 0, 0};
-    }
+    // keep LDS finite everywhere; the zeros must land before any direct load writes LDS
+    for (int i = lane; i < 2 * STAGE / 16; i += 64) *(u32x4*)(vl + i * 16) = u32x4{0, 0, 0, 0};
+    __syncthreads();
 
-    // query column -> (query row si, head h of this KV group)
-    const bool qvalid = col < p.nq;
-    const int si = qvalid ? col / p.group : 0;
-    const int h = g * p.group + (qvalid ? col % p.group : 0);
-    bf16x8 qf[KK];
-    {
+    // query columns cb*16 + c16 -> (query row, head of this KV group)
+    bf16x8 qf[CB][KQ];
+    int lim[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int colq = cb * 16 + c16;
+        const bool ok = colq < p.nq;
+        const int si = ok ? colq / p.group : 0;
+        const int h = g * p.group + (ok ? colq % p.group : 0);
         const uint16_t* qrow = p.q + ((size_t)(b * p.Sq + si) * p.Hq + h) * DK;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+        for (int kk = 0; kk < KQ; ++kk) {
+            const int dk0 = kk * 32 + grp * 8;
             u32x4 w = {0, 0, 0, 0};
-            if (qvalid) w = *(const u32x4*)(qrow + (2 * kk + half) * 8);
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
+            if (ok && dk0 < DK) w = *(const u32x4*)(qrow + dk0);
+            qf[cb][kk] = __builtin_bit_cast(bf16x8, w);
         }
+        lim[cb] = min(end - 1, p.causal ? L - p.Sq + si : L - 1);  // last key this column may see
     }
-    // last key this query row may see (bottom-right causal), and the split end
-    const int lim = min(end - 1, p.causal ? L - p.Sq + si : L - 1);
 
-    const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
-    auto row_ptr_k = [&](int key) -> const uint16_t* {
-        const int blk = table[key >> p.bs_log2];
-        return p.kc + (((size_t)blk * p.Hkv + g) * bs + (key & (bs - 1))) * DK;
+    // A 32-key step (32-aligned) lies in at most two cache blocks; their table
+    // entries are read with wave-uniform (scalar) loads so that only K and V
+    // loads sit in the vector-memory queue. Keys past L are clamped to L - 1
+    // (in the same step) so every load is issued and reads finite data.
+    const int lastb = (L - 1) >> p.bs_log2;
+    const __attribute__((address_space(4))) int32_t* ctable =
+        (const __attribute__((address_space(4))) int32_t*)table;  // read-only: scalar loads
+    auto step_blocks = [&](int k0, int& blkA, int& blkB) {
+        blkA = ctable[k0 >> p.bs_log2];
+        blkB = ctable[min((k0 + 16) >> p.bs_log2, lastb)];
     };
-    auto row_ptr_v = [&](int key) -> const uint16_t* {
-        const int blk = table[key >> p.bs_log2];
-        return p.vc + (((size_t)blk * p.Hkv + g) * bs + (key & (bs - 1))) * DV;
+    auto row_off = [&](int k0, int key, int blkA, int blkB) -> size_t {
+        key = min(key, L - 1);
+        const int blk = (key - k0) < 16 ? blkA : blkB;
+        return ((size_t)blk * p.Hkv + g) * bs + (key & (bs - 1));
     };
-
-    f32x16 oacc[DB];
+    // K fragments of step k0: block kb, k-step kk: key k0 + kb*16 + c16, dk kk*32 + grp*8
+    auto kload = [&](int k0, int blkA, int blkB, u32x4 (&kr)[2][KQ]) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d) oacc[d] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.f;
-    const int trow = (lane & 15) >> 2;
-    const int tcol = ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-
-    for (int k0 = start; k0 < end; k0 += 32) {
-        // K fragments of key k0 + col, straight into operand registers
-        bf16x8 kf[KK];
-        {
-            const int key = k0 + col;
-            const bool ok = key < end;
-            const uint16_t* kr = ok ? row_ptr_k(key) : p.kc;
+        for (int kb = 0; kb < 2; ++kb) {
+            const uint16_t* r = p.kc + row_off(k0, k0 + kb * 16 + c16, blkA, blkB) * DK;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                u32x4 w = {0, 0, 0, 0};
-                if (ok) w = *(const u32x4*)(kr + (2 * kk + half) * 8);
-                kf[kk] = __builtin_bit_cast(bf16x8, w);
+            for (int kk = 0; kk < KQ; ++kk) {
+                const int dk0 = kk * 32 + grp * 8;
+                if (dk0 < DK)
+                    kr[kb][kk] = *(const u32x4*)(r + dk0);
+                else
+                    kr[kb][kk] = u32x4{0, 0, 0, 0};
             }
         }
-        // V block of 32 keys into LDS (swizzled rows)
-        u32x4 vreg[LV];
+    };
+    // V rows of step k0 into stage st (swizzled 16-byte chunks)
+    auto vload = [&](int k0, int blkA, int blkB, int st) {
 #pragma unroll
-        for (int i = 0; i < LV; ++i) {
-            const int idx = lane + i * 64;
-            const int r = idx / NCVG, c = idx % NCVG;
-            const int key = k0 + r;
-            u32x4 w = {0, 0, 0, 0};
-            if (idx < 32 * NCVG && key < end) w = *(const u32x4*)(row_ptr_v(key) + c * 8);
-            vreg[i] = w;
+        for (int s = 0; s < VSEG; ++s) {
+            const int off = s * 1024 + lane * 16;
+            const int r = off / VROW;
+            const int c = ((off % VROW) >> 4) ^ swz<NCV>(r);
+            load_lds16(p.vc + row_off(k0, k0 + r, blkA, blkB) * DV + c * 8, vl + st * STAGE + s * 1024);
         }
-        __syncthreads();  // previous step's transposing reads are done
-#pragma unroll
-        for (int i = 0; i < LV; ++i) {
-            const int idx = lane + i * 64;
-            const int r = idx / NCVG, c = idx % NCVG;
-            if (idx < 32 * NCVG) *(u32x4*)(vl + r * (DVP * 2) + ((c ^ swz<NCV>(r)) * 16)) = vreg[i];
-        }
+    };
+    constexpr int LOADS_PER_STEP = 2 * KQ + VSEG;  // vector-memory instructions issued per step
 
-        f32x16 sacc = f32x16{};
+    f32x4 oacc[CB][DBV];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sacc = mfma32x32x16(kf[kk], qf[kk], sacc);
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int d = 0; d < DBV; ++d) oacc[cb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[CB], l_run[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.f;
+    }
 
-        float tmax = -INFINITY;
+    // one 32-key step: S^T, online softmax, O^T += V^T P^T (K fragments in kc_, V in stage st)
+    auto compute = [&](int k0, const u32x4 (&kc_)[2][KQ], int st) {
+        const char* vt = vl + st * STAGE;
+
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float x = sacc[i];
-            if (p.softcap_on) {
-                const float e = exp2_fast(x * p.c_tanh);
-                x = (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f)) * p.c_cap;
-            } else {
-                x *= p.c_score;
+        for (int cb = 0; cb < CB; ++cb) {
+            // S^T for 32 keys: two 16-key blocks
+            f32x4 sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KQ; ++kk)
+                    sacc[kb] = mfma16x16x32(__builtin_bit_cast(bf16x8, kc_[kb][kk]), qf[cb][kk], sacc[kb]);
             }
-            const int key = k0 + (i >> 2) * 8 + half * 4 + (i & 3);
-            if (key > lim) x = -INFINITY;
-            sacc[i] = x;
-            tmax = fmaxf(tmax, x);
-        }
-        tmax = halfwave_max(tmax);
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        m_run = m_new;
-        uint32_t pk[8];
-        float psum = 0.f;
+            float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t w = pack_bf16x2(exp2_fast(sacc[2 * j] - m_use), exp2_fast(sacc[2 * j + 1] - m_use));
-            pk[j] = w;
-            psum += bf16lo_to_f32(w) + bf16hi_to_f32(w);
-        }
-        l_run = l_run * alpha + psum;
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int d = 0; d < DB; ++d) oacc[d] *= alpha;
-
-        __syncthreads();  // V block visible to every lane
+                for (int i = 0; i < 4; ++i) {
+                    float x = sacc[kb][i];
+                    if (p.softcap_on) {
+                        const float e = exp2_fast(x * p.c_tanh);
+                        x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
+                    } else {
+                        x *= p.c_score;
+                    }
+                    if (k0 + kb * 16 + grp * 4 + i > lim[cb]) x = -INFINITY;
+                    sacc[kb][i] = x;
+                    mx = fmaxf(mx, x);
+                }
+            }
+            mx = quarterwave_max(mx);
+            const bool upd = mx > m_run[cb] + kTau;
+            if (__builtin_amdgcn_ballot_w64(upd)) {
+                const float alpha = upd ? exp2_fast(m_run[cb] - mx) : 1.f;
+                m_run[cb] = upd ? mx : m_run[cb];
+                l_run[cb] *= alpha;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const u32x4 pw = {pk[4 * jj], pk[4 * jj + 1], pk[4 * jj + 2], pk[4 * jj + 3]};
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-            const int ra = 16 * jj + half * 4 + trow;
-            const int rb = ra + 8;
+                for (int d = 0; d < DBV; ++d) oacc[cb][d] *= alpha;
+            }
+            const float nm = (m_run[cb] == -INFINITY) ? 0.f : -m_run[cb];
+            // P^T operand: keys (grp*4 + i) of block 0 then of block 1
+            uint32_t pk[4];
 #pragma unroll
-            for (int d = 0; d < DB; ++d) {
-                const int dc = d * 32 + tcol;
+            for (int kb = 0; kb < 2; ++kb) {
+                pk[2 * kb] = pack_bf16x2(exp2_fast(sacc[kb][0] + nm), exp2_fast(sacc[kb][1] + nm));
+                pk[2 * kb + 1] = pack_bf16x2(exp2_fast(sacc[kb][2] + nm), exp2_fast(sacc[kb][3] + nm));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) l_run[cb] = add_bf16x2(pk[j], l_run[cb]);
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+            // O^T += V^T P^T: V^T rows are keys grp*4 + 0..3 (block 0) and 16 + grp*4 + 0..3 (block 1)
+            const int ra = grp * 4 + (c16 >> 2);
+            const int rb = ra + 16;
+#pragma unroll
+            for (int d = 0; d < DBV; ++d) {
+                const int dc = d * 16 + (c16 & 3) * 4;
                 const int ch = dc >> 3, within = (dc & 7) * 2;
-                const bf16x4 va = lds_read_tr16(vl + ra * (DVP * 2) + ((ch ^ swz<NCV>(ra)) * 16) + within);
-                const bf16x4 vb = lds_read_tr16(vl + rb * (DVP * 2) + ((ch ^ swz<NCV>(rb)) * 16) + within);
-                const bf16x8 a = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[d] = mfma32x32x16(a, pb, oacc[d]);
+                const bf16x4 va = lds_read_tr16(vt + ra * VROW + ((ch ^ swz<NCV>(ra)) * 16) + within);
+                const bf16x4 vb = lds_read_tr16(vt + rb * VROW + ((ch ^ swz<NCV>(rb)) * 16) + within);
+                oacc[cb][d] = mfma16x16x32(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[cb][d]);
             }
         }
+    };
+    // wait until at most `pending` vector-memory instructions are in flight
+    auto wait_for_step = [&](bool more) {
+        if (more)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_STEP) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto prefetch = [&](int k0, u32x4 (&kr)[2][KQ], int st) {
+        int bA, bB;
+        step_blocks(k0, bA, bB);
+        kload(k0, bA, bB, kr);
+        vload(k0, bA, bB, st);
+    };
+
+    // Two K register buffers alternate (the loop is unrolled by two so no
+    // buffer is ever copied while its loads may still be in flight).
+    u32x4 kA[2][KQ], kB[2][KQ];
+    const int nsteps = (end - start + 31) / 32;
+    prefetch(start, kA, 0);
+    for (int it = 0; it < nsteps; it += 2) {
+        const int k0 = start + it * 32;
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more1 = it + 1 < nsteps;
+        if (more1) prefetch(k0 + 32, kB, 1);
+        wait_for_step(more1);
+        compute(k0, kA, 0);
+        if (!more1) break;
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more2 = it + 2 < nsteps;
+        if (more2) prefetch(k0 + 64, kA, 0);
+        wait_for_step(more2);
+        compute(k0 + 32, kB, 1);
     }
 
-    const float l_tot = halfwave_sum(l_run);
-    if (qvalid) {
-        const size_t row = (size_t)(b * p.Sq + si) * p.Hq + h;
-        const size_t slot = row * p.n_split + split;
-        if (half == 0) {
-            p.ws_ml[slot * 2] = m_run;
-            p.ws_ml[slot * 2 + 1] = l_tot;
-        }
-        float* op = p.ws_o + slot * DV;
 #pragma unroll
-        for (int d = 0; d < DB; ++d) {
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int dd = d * 32 + a4 * 8 + half * 4;
-                if (dd < DV)
-                    *(f32x4*)(op + dd) = f32x4{oacc[d][4 * a4], oacc[d][4 * a4 + 1], oacc[d][4 * a4 + 2],
-                                               oacc[d][4 * a4 + 3]};
+    for (int cb = 0; cb < CB; ++cb) {
+        const float l_tot = quarterwave_sum(l_run[cb]);
+        const int colq = cb * 16 + c16;
+        if (colq < p.nq) {
+            const int si = colq / p.group;
+            const int h = g * p.group + colq % p.group;
+            const size_t row = (size_t)(b * p.Sq + si) * p.Hq + h;
+            const size_t slot = row * p.n_split + split;
+            if (grp == 0) {
+                p.ws_ml[slot * 2] = m_run[cb];
+                p.ws_ml[slot * 2 + 1] = l_tot;
             }
+            float* op = p.ws_o + slot * DV;
+#pragma unroll
+            for (int d = 0; d < DBV; ++d) *(f32x4*)(op + d * 16 + grp * 4) = oacc[cb][d];
         }
     }
 }
@@ -261,7 +319,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
 
 template <int DK, int DV>
 hipError_t launch_paged(const SplitParams& sp, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV>), grid, dim3(64), 0, stream, sp);
+    if (sp.nq <= 16)
+        hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 1>), grid, dim3(64), 0, stream, sp);
+    else
+        hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 2>), grid, dim3(64), 0, stream, sp);
     return hipGetLastError();
 }
 
@@ -282,8 +343,9 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
     (void)Hkv;
     (void)dk;
     DecodePlan pl;
-    pl.split_len = kSplitLen;
-    pl.n_split = Sk_max > 0 ? (Sk_max + kSplitLen - 1) / kSplitLen : 1;
+    // keys per split: long caches get long splits (fewer partial rows to merge)
+    pl.split_len = Sk_max >= 16384 ? 1024 : Sk_max >= 4096 ? 512 : 256;
+    pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;
     pl.n_rows = B * Sq * Hq;
     pl.ws_bytes = (size_t)pl.n_rows * pl.n_split * ((size_t)dv + 2) * sizeof(float);
     pl.ws_bytes = (pl.ws_bytes + 255) & ~(size_t)255;
@@ -314,6 +376,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     sp.bs_log2 = lg;
     sp.max_blocks = a.max_blocks;
     sp.n_split = pl.n_split;
+    sp.split_len = pl.split_len;
     sp.c_score = a.scale * kLog2eH;
     sp.softcap_on = a.softcap != 0.f;
     sp.c_tanh = sp.softcap_on ? 2.f * a.scale / a.softcap * kLog2eH : 0.f;
