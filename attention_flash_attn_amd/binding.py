@@ -101,6 +101,18 @@ def _ptr(t, name, dtype=None, allow_none=False):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _row_ptr(t, name):
+    """Row array of a gathered cache: rows may be strided, each row contiguous."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be a GPU tensor" % name)
+    if t.dtype != torch.bfloat16:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be bfloat16" % name)
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be [rows, width] with contiguous rows" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
 def _stream(stream):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -141,9 +153,10 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
                     sinks=None, block_table=None, seq_lens=None, row_index=None, key_pos=None,
                     q_pos=None, kv_row_stride=0, Hkv=None, dk=None, dv=None, stream=None):
     """Paged mode: k_cache [n_blocks,Hkv,bs,dk], v_cache [n_blocks,Hkv,bs,dv], block_table
-    [B,max_blocks] int32, seq_lens [B] int32. Gathered mode: k_cache / v_cache are row
-    arrays (any shape; dk, dv and kv_row_stride given), row_index [B,n_sel] int32,
-    key_pos [B,n_sel] fp32, q_pos [B] int32. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv]."""
+    [B,max_blocks] int32, seq_lens [B] int32. Gathered mode: k_cache / v_cache are 2-D row
+    views [rows, width] sharing one row stride (e.g. kv[:, :dk] and kv[:, 64:]), with
+    row_index [B,n_sel] int32, key_pos [B,n_sel] fp32, q_pos [B] int32; dk defaults to q's
+    width and dv to o's. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv]."""
     import torch
     lib = load_library()
     B, Sq, Hq, qdk = q.shape
@@ -161,8 +174,15 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
         dk = qdk if dk is None else dk
         dv = o.shape[3] if dv is None else dv
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.attn_decode_fwd(_ptr(q, "q", torch.bfloat16), _ptr(k_cache, "k_cache", torch.bfloat16),
-                             _ptr(v_cache, "v_cache", torch.bfloat16), _ptr(o, "o"), _odtype(o),
+    if paged:
+        kp, vp = _ptr(k_cache, "k_cache", torch.bfloat16), _ptr(v_cache, "v_cache", torch.bfloat16)
+    else:
+        kp, vp = _row_ptr(k_cache, "k_cache"), _row_ptr(v_cache, "v_cache")
+        if not kv_row_stride:
+            kv_row_stride = k_cache.stride(0)
+        if v_cache.stride(0) != kv_row_stride:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "k_cache and v_cache rows must share one stride")
+    st = lib.attn_decode_fwd(_ptr(q, "q", torch.bfloat16), kp, vp, _ptr(o, "o"), _odtype(o),
                              B, Hq, Hkv, Sq, int(Sk_max), dk, dv, float(scale), int(bool(causal)),
                              float(softcap), _ptr(sinks, "sinks", torch.float32, True),
                              _ptr(block_table, "block_table", torch.int32, True), bs, max_blocks,

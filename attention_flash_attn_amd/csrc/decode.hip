@@ -265,6 +265,204 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
     }
 }
 
+// Gathered mode: one workgroup per (key split, group of NW*16 heads, token).
+// The selected rows of the token are gathered straight from the row cache in
+// their native layout (the approach of the "MLA Decode Attention Kernel API
+// Reference" page, Background: no pre-gathered copy), 32 rows per step, into
+// an LDS double buffer shared by the NW waves; each wave owns 16 heads (the
+// query columns of its 16x16x32 MFMAs) and the whole value width. When the
+// value is a prefix of the key row (v_cache == k_cache) the rows are loaded
+// once. A key is live iff its position is at or before the token's.
+struct GatherParams {
+    const uint16_t* __restrict__ q;
+    const uint16_t* __restrict__ kc;
+    const uint16_t* __restrict__ vc;
+    float* __restrict__ ws_o;
+    float* __restrict__ ws_ml;
+    const int32_t* __restrict__ row_index;
+    const float* __restrict__ key_pos;
+    const int32_t* __restrict__ q_pos;
+    int T, Hq, n_sel, n_split, split_len, v_is_k;
+    long long row_stride;  // elements
+    float c_score, c_tanh, c_cap;
+    int causal, softcap_on;
+};
+
+constexpr int kGatherMaxSplit = 1024;  // keys per split the LDS index table holds
+
+template <int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
+void decode_gathered_split_kernel(GatherParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int KQ = DK / 32;          // QK k-steps of 32
+    constexpr int DBV = DV / 16;         // 16-row blocks of O^T
+    constexpr int KROW = DK * 2, VROW = DV * 2;
+    constexpr int NCK = DK / 8, NCV = DV / 8;
+    constexpr int KSTAGE = 32 * KROW, VSTAGE = 32 * VROW;
+    constexpr int KSEG = KSTAGE / 1024, VSEG = VSTAGE / 1024;
+    static_assert(DK % 32 == 0 && DV % 16 == 0 && KSTAGE % 1024 == 0 && VSTAGE % 1024 == 0, "shape");
+    __shared__ __attribute__((aligned(1024))) char kst[2 * KSTAGE];
+    __shared__ __attribute__((aligned(1024))) char vst[2 * VSTAGE];
+    __shared__ int32_t srow[kGatherMaxSplit];
+    __shared__ float spos[kGatherMaxSplit];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, c16 = lane & 15;
+    const int split = blockIdx.x, hgrp = blockIdx.y, t = blockIdx.z;
+    const int start = split * p.split_len;
+    const int end = min(p.n_sel, start + p.split_len);
+    const int nk = end - start;
+    const float qpos = (float)p.q_pos[t];
+
+    // row indices and positions of this split, once; LDS starts finite
+    for (int i = tid; i < nk; i += NT) {
+        srow[i] = p.row_index[(size_t)t * p.n_sel + start + i];
+        spos[i] = p.key_pos[(size_t)t * p.n_sel + start + i];
+    }
+    for (int i = tid; i < 2 * KSTAGE / 16; i += NT) *(u32x4*)(kst + i * 16) = u32x4{0, 0, 0, 0};
+    if (!p.v_is_k)
+        for (int i = tid; i < 2 * VSTAGE / 16; i += NT) *(u32x4*)(vst + i * 16) = u32x4{0, 0, 0, 0};
+    __syncthreads();
+
+    const int h = hgrp * (NW * 16) + wave * 16 + c16;  // this lane's head (query column)
+    const bool hok = h < p.Hq;
+    bf16x8 qf[KQ];
+    {
+        const uint16_t* qrow = p.q + ((size_t)t * p.Hq + (hok ? h : 0)) * DK;
+#pragma unroll
+        for (int kk = 0; kk < KQ; ++kk) {
+            u32x4 w = {0, 0, 0, 0};
+            if (hok) w = *(const u32x4*)(qrow + kk * 32 + grp * 8);
+            qf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    // rows of step i into stage st: every wave issues every NW-th 1 KB segment
+    auto issue = [&](int i, int st) {
+        const int r0 = i * 32;
+#pragma unroll
+        for (int j = 0; j < (KSEG + NW - 1) / NW; ++j) {
+            const int s = wave + j * NW;
+            if (s < KSEG) {
+                const int off = s * 1024 + lane * 16;
+                const int r = off / KROW;
+                const int c = ((off % KROW) >> 4) ^ swz<NCK>(r);
+                const int kr = min(r0 + r, nk - 1);  // rows past the split repeat its last row (finite, masked)
+                load_lds16(p.kc + (size_t)srow[kr] * p.row_stride + c * 8, kst + st * KSTAGE + s * 1024);
+            }
+        }
+        if (!p.v_is_k) {
+#pragma unroll
+            for (int j = 0; j < (VSEG + NW - 1) / NW; ++j) {
+                const int s = wave + j * NW;
+                if (s < VSEG) {
+                    const int off = s * 1024 + lane * 16;
+                    const int r = off / VROW;
+                    const int c = ((off % VROW) >> 4) ^ swz<NCV>(r);
+                    const int kr = min(r0 + r, nk - 1);
+                    load_lds16(p.vc + (size_t)srow[kr] * p.row_stride + c * 8, vst + st * VSTAGE + s * 1024);
+                }
+            }
+        }
+    };
+
+    f32x4 oacc[DBV];
+#pragma unroll
+    for (int d = 0; d < DBV; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int nsteps = (nk + 31) / 32;
+    if (nsteps > 0) issue(0, 0);
+    for (int i = 0; i < nsteps; ++i) {
+        wait_vmem();
+        __syncthreads();
+        if (i + 1 < nsteps) issue(i + 1, (i + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const char* kt = kst + (i & 1) * KSTAGE;
+        const char* vt = p.v_is_k ? kt : vst + (i & 1) * VSTAGE;
+        const int vrow = p.v_is_k ? KROW : VROW;
+        const int r0 = i * 32;
+
+        // S^T: two 16-key blocks; A = K rows (key c16 of the block), k-step kk
+        f32x4 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int r = kb * 16 + c16;
+            const char* krow = kt + r * KROW;
+#pragma unroll
+            for (int kk = 0; kk < KQ; ++kk) {
+                const int c = kk * 4 + grp;
+                const bf16x8 a = *(const bf16x8*)(krow + ((c ^ swz<NCK>(r)) * 16));
+                sacc[kb] = mfma16x16x32(a, qf[kk], sacc[kb]);
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = sacc[kb][e];
+                if (p.softcap_on) {
+                    const float ex = exp2_fast(x * p.c_tanh);
+                    x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(ex + 1.f);
+                } else {
+                    x *= p.c_score;
+                }
+                const int kl = r0 + kb * 16 + grp * 4 + e;  // key within the split
+                const bool live = kl < nk && (!p.causal || spos[kl] <= qpos);
+                if (!live) x = -INFINITY;
+                sacc[kb][e] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = quarterwave_max(mx);
+        const bool upd = mx > m_run + kTau;
+        if (__builtin_amdgcn_ballot_w64(upd)) {
+            const float alpha = upd ? exp2_fast(m_run - mx) : 1.f;
+            m_run = upd ? mx : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < DBV; ++d) oacc[d] *= alpha;
+        }
+        const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+        uint32_t pk[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            pk[2 * kb] = pack_bf16x2(exp2_fast(sacc[kb][0] + nm), exp2_fast(sacc[kb][1] + nm));
+            pk[2 * kb + 1] = pack_bf16x2(exp2_fast(sacc[kb][2] + nm), exp2_fast(sacc[kb][3] + nm));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l_run = add_bf16x2(pk[j], l_run);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        const int ra = grp * 4 + (c16 >> 2);
+        const int rb = ra + 16;
+        const int swzv = p.v_is_k ? 0 : 1;  // row swizzle of the V rows' stage
+#pragma unroll
+        for (int d = 0; d < DBV; ++d) {
+            const int dc = d * 16 + (c16 & 3) * 4;
+            const int ch = dc >> 3, within = (dc & 7) * 2;
+            const int cha = swzv ? (ch ^ swz<NCV>(ra)) : (ch ^ swz<NCK>(ra));
+            const int chb = swzv ? (ch ^ swz<NCV>(rb)) : (ch ^ swz<NCK>(rb));
+            const bf16x4 va = lds_read_tr16(vt + ra * vrow + cha * 16 + within);
+            const bf16x4 vb = lds_read_tr16(vt + rb * vrow + chb * 16 + within);
+            oacc[d] = mfma16x16x32(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[d]);
+        }
+    }
+
+    const float l_tot = quarterwave_sum(l_run);
+    if (hok) {
+        const size_t row = (size_t)t * p.Hq + h;
+        const size_t slot = row * p.n_split + split;
+        if (grp == 0) {
+            p.ws_ml[slot * 2] = m_run;
+            p.ws_ml[slot * 2 + 1] = l_tot;
+        }
+        float* op = p.ws_o + slot * DV;
+#pragma unroll
+        for (int d = 0; d < DBV; ++d) *(f32x4*)(op + d * 16 + grp * 4) = oacc[d];
+    }
+}
+
 struct CombineParams {
     const float* __restrict__ ws_o;
     const float* __restrict__ ws_ml;
@@ -326,10 +524,30 @@ hipError_t launch_paged(const SplitParams& sp, dim3 grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
+hipError_t launch_combine(const DecodeArgs& a, const DecodePlan& pl, float* ws_o, float* ws_ml,
+                          const int32_t* seq_lens, hipStream_t stream) {
+    CombineParams cp;
+    cp.ws_o = ws_o;
+    cp.ws_ml = ws_ml;
+    cp.seq_lens = seq_lens;
+    cp.sinks = a.sinks;
+    cp.o = a.o;
+    cp.Sq = a.Sq;
+    cp.Hq = a.Hq;
+    cp.n_split = pl.n_split;
+    cp.split_len = pl.split_len;
+    cp.dv = a.dv;
+    if (a.o_f32)
+        hipLaunchKernelGGL((decode_combine_kernel<true>), dim3((unsigned)pl.n_rows), dim3(64), 0, stream, cp);
+    else
+        hipLaunchKernelGGL((decode_combine_kernel<false>), dim3((unsigned)pl.n_rows), dim3(64), 0, stream, cp);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool decode_supported(int dk, int dv, bool gathered) {
-    if (gathered) return false;
+    if (gathered) return dk == 576 && dv == 512;
     switch (dk * 1000 + dv) {
         case 16016: case 32032: case 64064: case 96096: case 128128:
         case 192192: case 256256: case 192128:
@@ -383,8 +601,37 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     sp.c_cap = a.softcap * kLog2eH;
     sp.causal = a.causal;
 
-    const dim3 grid((unsigned)pl.n_split, (unsigned)a.Hkv, (unsigned)a.B);
     hipError_t e;
+    if (a.row_index != nullptr) {
+        GatherParams gp;
+        gp.q = (const uint16_t*)a.q;
+        gp.kc = (const uint16_t*)a.k_cache;
+        gp.vc = (const uint16_t*)a.v_cache;
+        gp.ws_o = ws_o;
+        gp.ws_ml = ws_ml;
+        gp.row_index = a.row_index;
+        gp.key_pos = a.key_pos;
+        gp.q_pos = a.q_pos;
+        gp.T = a.B;
+        gp.Hq = a.Hq;
+        gp.n_sel = a.n_sel;
+        gp.n_split = pl.n_split;
+        gp.split_len = pl.split_len;
+        gp.v_is_k = a.v_cache == a.k_cache;
+        gp.row_stride = a.row_stride;
+        gp.c_score = sp.c_score;
+        gp.c_tanh = sp.c_tanh;
+        gp.c_cap = sp.c_cap;
+        gp.causal = a.causal;
+        gp.softcap_on = sp.softcap_on;
+        constexpr int NW = 4;
+        const dim3 ggrid((unsigned)pl.n_split, (unsigned)((a.Hq + NW * 16 - 1) / (NW * 16)), (unsigned)a.B);
+        hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW>), ggrid, dim3(NW * 64), 0, stream, gp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_combine(a, pl, ws_o, ws_ml, nullptr, stream);
+    }
+    const dim3 grid((unsigned)pl.n_split, (unsigned)a.Hkv, (unsigned)a.B);
     switch (a.dk * 1000 + a.dv) {
         case 16016: e = launch_paged<16, 16>(sp, grid, stream); break;
         case 32032: e = launch_paged<32, 32>(sp, grid, stream); break;
@@ -398,22 +645,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     }
     if (e != hipSuccess) return e;
 
-    CombineParams cp;
-    cp.ws_o = ws_o;
-    cp.ws_ml = ws_ml;
-    cp.seq_lens = a.seq_lens;
-    cp.sinks = a.sinks;
-    cp.o = a.o;
-    cp.Sq = a.Sq;
-    cp.Hq = a.Hq;
-    cp.n_split = pl.n_split;
-    cp.split_len = pl.split_len;
-    cp.dv = a.dv;
-    if (a.o_f32)
-        hipLaunchKernelGGL((decode_combine_kernel<true>), dim3((unsigned)pl.n_rows), dim3(64), 0, stream, cp);
-    else
-        hipLaunchKernelGGL((decode_combine_kernel<false>), dim3((unsigned)pl.n_rows), dim3(64), 0, stream, cp);
-    return hipGetLastError();
+    return launch_combine(a, pl, ws_o, ws_ml, a.seq_lens, stream);
 }
 
 }  // namespace attn

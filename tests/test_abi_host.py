@@ -96,6 +96,8 @@ def decode(lib, **kw):
     (dict(Hq=64, Hkv=1), 2),                                # group of 64 > 32 query columns
     (dict(dk=100, dv=100), 2),
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, Hkv=2, Hq=8), 1),
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=128), 2),          # gathered (128,128)
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=576, dk=576, dv=512, Sq=2), 1),
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=99, stride=128), 1),
     (dict(table=None, rows=FAKE, kpos=None, qpos=FAKE, n_sel=100, stride=128), 1),
 ])
@@ -105,8 +107,11 @@ def test_decode_rejects(kw, status):
 
 
 def test_workspace_bytes():
-    # 512-key splits: ceil(32768/512) = 64 splits, (dv + 2) floats per row per split
+    # 32768 keys use 1024-key splits: 32 splits, (dv + 2) floats per row per split
     n = attn.attn_decode_workspace_bytes(64, 64, 8, 1, 32768, 128, 128)
-    assert n >= 64 * 64 * 64 * 130 * 4
+    assert n >= 64 * 64 * 32 * 130 * 4
+    # 2048 keys use 256-key splits: 8 splits
+    n = attn.attn_decode_workspace_bytes(16, 128, 1, 1, 2048, 576, 512)
+    assert n >= 16 * 128 * 8 * 514 * 4
     assert attn.attn_decode_workspace_bytes(0, 64, 8, 1, 100, 128, 128) == 0
     assert attn.attn_decode_workspace_bytes(2, 6, 4, 1, 100, 128, 128) == 0

@@ -93,3 +93,65 @@ def test_config4_full_size_sampled():
                                 case["seq_lens"], c["scale"], batches=batches)
     err, cos = check_close(host(o)[batches], ro, "bf16", "config 4")
     print("config 4 sampled: max err %.3g cos %.8f" % (err, cos))
+
+
+# ---------------------------------------------------------------- gathered rows (MLA-style)
+def run_gathered(case, Hq, dk, dv, scale, causal=True, softcap=0.0, sinks=None, o_dtype="bf16", v_offset=0):
+    kv = dev_bf16(case["kv"])
+    q = dev_bf16(case["q"]).view(case["q"].shape[0], 1, Hq, dk)
+    T, n_sel = case["row_index"].shape
+    o = torch.empty((T, 1, Hq, dv), device="cuda", dtype=torch.float32 if o_dtype == "f32" else torch.bfloat16)
+    nbytes = binding.attn_decode_workspace_bytes(T, Hq, 1, 1, n_sel, dk, dv)
+    ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
+    k_rows = kv[:, :dk] if v_offset == 0 else kv[:, :dk]
+    v_rows = kv[:, v_offset:v_offset + dv]
+    binding.attn_decode_fwd(q, k_rows, v_rows, o, ws, scale=scale, Sk_max=n_sel, causal=causal, softcap=softcap,
+                            sinks=None if sinks is None else dev(sinks), row_index=dev(case["row_index"]),
+                            key_pos=dev(case["key_pos"]), q_pos=dev(case["q_pos"]), dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return o[:, 0]
+
+
+def check_gathered(T, Hq, n_rows, n_sel, causal=True, softcap=0.0, sinks=False, o_dtype="f32", future=0,
+                   v_offset=0, seed=300, shuffle=False):
+    dk, dv = 576, 512
+    print("gathered T=%d Hq=%d rows=%d n_sel=%d causal=%d softcap=%g sinks=%d %s future=%d v_offset=%d" %
+          (T, Hq, n_rows, n_sel, causal, softcap, sinks, o_dtype, future, v_offset), flush=True)
+    case = synth.gathered_case(seed, T, Hq, dk, dv, n_rows, n_sel, row_dim=576, sinks=sinks, future_keys=future)
+    if shuffle:
+        perm = np.random.default_rng(seed).permutation(n_sel)
+        case["row_index"] = np.ascontiguousarray(case["row_index"][:, perm])
+        case["key_pos"] = np.ascontiguousarray(case["key_pos"][:, perm])
+    scale = 1.0 / math.sqrt(dk)
+    o = run_gathered(case, Hq, dk, dv, scale, causal, softcap, case["sinks"], o_dtype, v_offset)
+    kv = case["kv"]
+    ro, _ = oracle.decode_gathered(case["q"], kv[:, :dk], kv[:, v_offset:v_offset + dv], case["row_index"],
+                                   case["key_pos"], case["q_pos"], scale, causal=causal, softcap=softcap,
+                                   sinks=case["sinks"])
+    return check_close(host(o), ro, o_dtype, "gathered decode")
+
+
+def test_gathered_small_and_ragged():
+    check_gathered(3, 64, 4096, 300)                                  # ragged last split
+    check_gathered(2, 20, 2048, 65, o_dtype="bf16", seed=301)         # heads not a multiple of 16
+    check_gathered(2, 128, 4096, 1, seed=302)                         # a single selected row
+
+
+def test_gathered_position_mask():
+    check_gathered(4, 32, 8192, 512, future=64, seed=303)             # 64 keys per token lie after it
+    check_gathered(2, 32, 8192, 512, causal=False, future=64, seed=304)
+
+
+def test_gathered_softcap_sinks_order_and_layout():
+    check_gathered(2, 64, 4096, 700, softcap=30.0, sinks=True, seed=305)
+    check_gathered(2, 64, 4096, 700, shuffle=True, seed=306)          # selection order does not matter
+    # value stored after a 64-wide field ([k_pe | latent] rows): v = row[64:576], k = row[0:576]
+    case_rows = 4096
+    check_gathered(2, 32, case_rows, 333, v_offset=64, seed=307)
+
+
+def test_config5_full_size():
+    c = synth.CONFIGS["c5_gathered_mla_decode"]
+    print("full-size c5 gathered decode", flush=True)
+    err, cos = check_gathered(c["T"], c["Hq"], c["n_rows"], c["n_sel"], o_dtype="bf16", seed=c["seed"])
+    print("config 5: max err %.3g cos %.8f" % (err, cos))
