@@ -114,15 +114,27 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
         (ATTN_LDS bf16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
 
-// 16-byte chunk swizzle inside an LDS row of nch chunks. Rows r..r+7 map a
-// given chunk to 8 different 16-byte bank groups (conflict-free 128-bit reads
-// of one column chunk by consecutive rows), and rows 4a..4a+3 map an aligned
-// chunk pair to 4 different 32-byte bank groups (conflict-free transposing
-// reads of 4 rows x 16 columns).
-template <int NCH>
+// 16-byte chunk swizzle of LDS rows holding NCH chunks. The LDS serves 256
+// bytes per cycle (64 banks of 4 bytes); a row's logical chunk c is stored at
+// c ^ swz(r) so that the reads each kernel issues are conflict-free:
+//  * 32x32 MFMA operands (MF16 = false): a 128-bit read of one chunk by 16
+//    consecutive rows, and a transposing read of 4 aligned rows x 64 bytes;
+//  * 16x16 MFMA operands (MF16 = true): a 128-bit read of one chunk by 16
+//    consecutive rows, and a transposing read of 8 aligned rows x 32 bytes.
+// Rows whose pitch is a multiple of 256 bytes use a 4-bit XOR; pitches that
+// are 128 bytes mod 256 (consecutive rows start half a bank row apart) a
+// 3-bit XOR; the swizzle never leaves the row.
+template <int NCH, bool MF16 = false>
 __device__ __forceinline__ int swz(int r) {
-    constexpr int mask = (NCH % 8 == 0) ? 7 : (NCH % 4 == 0) ? 3 : (NCH % 2 == 0) ? 1 : 0;
-    return (((r & 3) << 1) | ((r >> 2) & 1)) & mask;
+    constexpr int pitch = NCH * 16;
+    if constexpr (pitch % 256 == 0) {
+        return MF16 ? (((r & 7) << 1) | ((r >> 3) & 1)) : (((r & 3) << 2) | ((r >> 2) & 3));
+    } else if constexpr (pitch % 128 == 0) {
+        return MF16 ? ((((r >> 1) & 3) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    } else {
+        constexpr int mask = (NCH % 4 == 0) ? 3 : (NCH % 2 == 0) ? 1 : 0;
+        return (((r & 3) << 1) | ((r >> 2) & 1)) & mask;
+    }
 }
 
 }  // namespace attn

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
         for (int s = 0; s < VSEG; ++s) {
             const int off = s * 1024 + lane * 16;
             const int r = off / VROW;
-            const int c = ((off % VROW) >> 4) ^ swz<NCV>(r);
+            const int c = ((off % VROW) >> 4) ^ swz<NCV, true>(r);
             load_lds16(p.vc + row_off(k0, k0 + r, blkA, blkB) * DV + c * 8, vl + st * STAGE + s * 1024);
         }
     };
@@ -204,8 +204,8 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
             for (int d = 0; d < DBV; ++d) {
                 const int dc = d * 16 + (c16 & 3) * 4;
                 const int ch = dc >> 3, within = (dc & 7) * 2;
-                const bf16x4 va = lds_read_tr16(vt + ra * VROW + ((ch ^ swz<NCV>(ra)) * 16) + within);
-                const bf16x4 vb = lds_read_tr16(vt + rb * VROW + ((ch ^ swz<NCV>(rb)) * 16) + within);
+                const bf16x4 va = lds_read_tr16(vt + ra * VROW + ((ch ^ swz<NCV, true>(ra)) * 16) + within);
+                const bf16x4 vb = lds_read_tr16(vt + rb * VROW + ((ch ^ swz<NCV, true>(rb)) * 16) + within);
                 oacc[cb][d] = mfma16x16x32(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[cb][d]);
             }
         }
@@ -345,7 +345,7 @@ void decode_gathered_split_kernel(GatherParams p) {
             if (s < KSEG) {
                 const int off = s * 1024 + lane * 16;
                 const int r = off / KROW;
-                const int c = ((off % KROW) >> 4) ^ swz<NCK>(r);
+                const int c = ((off % KROW) >> 4) ^ swz<NCK, true>(r);
                 const int kr = min(r0 + r, nk - 1);  // rows past the split repeat its last row (finite, masked)
                 load_lds16(p.kc + (size_t)srow[kr] * p.row_stride + c * 8, kst + st * KSTAGE + s * 1024);
             }
@@ -357,7 +357,7 @@ void decode_gathered_split_kernel(GatherParams p) {
                 if (s < VSEG) {
                     const int off = s * 1024 + lane * 16;
                     const int r = off / VROW;
-                    const int c = ((off % VROW) >> 4) ^ swz<NCV>(r);
+                    const int c = ((off % VROW) >> 4) ^ swz<NCV, true>(r);
                     const int kr = min(r0 + r, nk - 1);
                     load_lds16(p.vc + (size_t)srow[kr] * p.row_stride + c * 8, vst + st * VSTAGE + s * 1024);
                 }
@@ -392,7 +392,7 @@ void decode_gathered_split_kernel(GatherParams p) {
 #pragma unroll
             for (int kk = 0; kk < KQ; ++kk) {
                 const int c = kk * 4 + grp;
-                const bf16x8 a = *(const bf16x8*)(krow + ((c ^ swz<NCK>(r)) * 16));
+                const bf16x8 a = *(const bf16x8*)(krow + ((c ^ swz<NCK, true>(r)) * 16));
                 sacc[kb] = mfma16x16x32(a, qf[kk], sacc[kb]);
             }
         }
@@ -441,8 +441,8 @@ void decode_gathered_split_kernel(GatherParams p) {
         for (int d = 0; d < DBV; ++d) {
             const int dc = d * 16 + (c16 & 3) * 4;
             const int ch = dc >> 3, within = (dc & 7) * 2;
-            const int cha = swzv ? (ch ^ swz<NCV>(ra)) : (ch ^ swz<NCK>(ra));
-            const int chb = swzv ? (ch ^ swz<NCV>(rb)) : (ch ^ swz<NCK>(rb));
+            const int cha = swzv ? (ch ^ swz<NCV, true>(ra)) : (ch ^ swz<NCK, true>(ra));
+            const int chb = swzv ? (ch ^ swz<NCV, true>(rb)) : (ch ^ swz<NCK, true>(rb));
             const bf16x4 va = lds_read_tr16(vt + ra * vrow + cha * 16 + within);
             const bf16x4 vb = lds_read_tr16(vt + rb * vrow + chb * 16 + within);
             oacc[d] = mfma16x16x32(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[d]);

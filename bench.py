@@ -189,6 +189,55 @@ def main():
         },
     }
 
+    # ---------------- gathered-row decode (MLA shape), timed cold: 8 copies of the row
+    # cache rotate so the selected rows (37.7 MB per call) cannot stay in the 256 MB MALL
+    c5 = synth.CONFIGS["c5_gathered_mla_decode"]
+    log("generating gathered decode inputs")
+    gc = synth.gathered_case(c5["seed"], c5["T"], c5["Hq"], c5["dk"], c5["dv"], c5["n_rows"], c5["n_sel"],
+                             row_dim=c5["row_dim"])
+    ncopy = 8
+    kv5 = [to_dev(gc["kv"]) for _ in range(ncopy)]
+    q5 = to_dev(gc["q"]).view(c5["T"], 1, c5["Hq"], c5["dk"])
+    ri5 = torch.from_numpy(gc["row_index"]).to(dev)
+    kp5 = torch.from_numpy(gc["key_pos"]).to(dev)
+    qp5 = torch.from_numpy(gc["q_pos"]).to(dev)
+    o5 = torch.empty((c5["T"], 1, c5["Hq"], c5["dv"]), device=dev, dtype=torch.bfloat16)
+    ws5 = torch.empty(binding.attn_decode_workspace_bytes(c5["T"], c5["Hq"], 1, 1, c5["n_sel"], c5["dk"], c5["dv"]),
+                      device=dev, dtype=torch.uint8)
+    bytes5 = (c5["T"] * c5["n_sel"] * c5["row_dim"] * 2 + ri5.numel() * 4 + kp5.numel() * 4 + qp5.numel() * 4 +
+              q5.numel() * 2 + o5.numel() * 2)
+    flops5 = 2.0 * c5["T"] * c5["Hq"] * c5["n_sel"] * (c5["dk"] + c5["dv"])
+
+    def gathered(i):
+        kv = kv5[i % ncopy]
+        binding.attn_decode_fwd(q5, kv[:, :c5["dk"]], kv[:, :c5["dv"]], o5, ws5, scale=c5["scale"],
+                                Sk_max=c5["n_sel"], causal=True, row_index=ri5, key_pos=kp5, q_pos=qp5)
+    for i in range(ncopy):
+        gathered(i)
+    reps = 8 * ncopy
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        gathered(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t5 = e0.elapsed_time(e1) * 1e-3 / reps
+    log("gathered decode c5: %.2f us/call, %.1f GB/s (%.1f%% of HBM peak), %.1f TFLOP/s" %
+        (t5 * 1e6, bytes5 / t5 / 1e9, 100 * bytes5 / t5 / 1e9 / PEAK_HBM_GBS, flops5 / t5 / 1e12))
+    result["decode_gathered"] = {
+        "workload": "16 tokens x 128 heads, 2048 gathered rows of 576 (key) / first 512 (value), "
+                    "65536-row cache in permuted 64-row blocks, causal on position, bf16 out, cold (8 rotated "
+                    "cache copies)",
+        "value": round(bytes5 / t5 / 1e9, 1), "unit": "GB/s", "us_per_call": round(t5 * 1e6, 2),
+        "bytes_per_call": bytes5, "flops_per_call": flops5,
+        "roofline": {"kernel": "decode_gathered_split_kernel<576,512,4> + decode_combine_kernel", "bound": "hbm",
+                     "achieved": round(bytes5 / t5 / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(bytes5 / t5 / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "mfma_frac": round(flops5 / t5 / 1e12 / PEAK_BF16_TFLOPS, 4)},
+    }
+    del kv5, gc
+
     # ---------------- other workloads (own timing, after the step loop)
     if not args.no_other:
         other = {}
