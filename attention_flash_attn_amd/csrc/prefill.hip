@@ -59,6 +59,14 @@ struct PrefillParams {
 
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
+// LDS fragment reads issued ahead of their MFMA (K: 128-bit reads, V: transposing pairs)
+#ifndef ATTN_PF_K
+#define ATTN_PF_K 4
+#endif
+#ifndef ATTN_PF_V
+#define ATTN_PF_V 4
+#endif
+
 // Tile configurations (keys per tile, waves per workgroup, target waves per SIMD)
 #ifndef ATTN_D128_CFG
 #define ATTN_D128_CFG 64, 4, 2
@@ -201,7 +209,7 @@ void prefill_kernel(PrefillParams p) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // S^T = K Q^T; K fragments are read from LDS PF steps ahead of their MFMA
         constexpr int NQK = KB * KK;
-        constexpr int PFK = NQK < 4 ? NQK : 4;
+        constexpr int PFK = NQK < ATTN_PF_K ? NQK : ATTN_PF_K;
         auto kload = [&](int idx) -> bf16x8 {
             const int kb = idx / KK, kk = idx % KK;
             return *(const bf16x8*)(kt + kofs + kk * (BN * 32) + kb * 1024);
@@ -276,7 +284,7 @@ void prefill_kernel(PrefillParams p) {
         }
         // O^T += V^T P^T, 16 keys per MFMA; V^T fragments read PF steps ahead
         constexpr int NPV = KB * 2 * DB;
-        constexpr int PFV = NPV < 4 ? NPV : 4;
+        constexpr int PFV = NPV < ATTN_PF_V ? NPV : ATTN_PF_V;
         auto vload = [&](int idx) -> bf16x8 {
             const int d = idx % DB, jj = (idx / DB) % 2, kb = idx / (2 * DB);
             const char* pa = vt + vofs + d * (BN * 64) + kb * 2048 + jj * 1024;
