@@ -33,6 +33,26 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE passes (read counter
+# scaled x2, write x1 against a 1 GiB plain copy; see profiles/hbm_traffic_bench.md), valid
+# only while the kernel sources hash to the values they were measured on.
+MEASURED_TRAFFIC = {
+    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp"), "sha256_16": "37db552b9bd46eb8", "bytes": 787957435},
+    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp"), "sha256_16": "2376ea25efe294a3", "bytes": 5072994742},
+    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp"), "sha256_16": "2376ea25efe294a3", "bytes": 123889606},
+}
+
+
+def measured_traffic(key):
+    """The recorded traffic if the kernel sources are unchanged since the counters were taken."""
+    import hashlib
+    e = MEASURED_TRAFFIC[key]
+    m = hashlib.sha256()
+    for f in e["sources"]:
+        with open(os.path.join(ROOT, "attention_flash_attn_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return e["bytes"] if m.hexdigest()[:16] == e["sha256_16"] else None
+
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
@@ -57,6 +77,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-other", action="store_true", help="skip the extra workloads")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) pairs in the CPU sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (a plain copy kernel of known size, "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the kernels shard over "
@@ -110,6 +133,18 @@ def main():
                                 block_table=table4, seq_lens=lens4)
 
     stream = torch.cuda.current_stream()
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB in %.1f us (%.0f GB/s read+write)" %
+            (c0.elapsed_time(c1) * 1e3, 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9))
+        del src, dst
     for _ in range(args.warmup):
         prefill()
         decode()
@@ -174,7 +209,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill_c2"),
             "avg_launch_us": round(avg_pre * 1e6, 2),
             "back_to_back_TFLOP/s": round(flops2 / t_b2b / 1e12, 2),
             "back_to_back_us": round(t_b2b * 1e6, 2),
@@ -185,7 +220,7 @@ def main():
             "us_per_call": round(avg_dec * 1e6, 2),
             "roofline": {"kernel": "decode_paged_split_kernel<128,128> + decode_combine_kernel", "bound": "hbm",
                          "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_c4")},
         },
     }
 
@@ -233,7 +268,7 @@ def main():
         "bytes_per_call": bytes5, "flops_per_call": flops5,
         "roofline": {"kernel": "decode_gathered_split_kernel<576,512,4> + decode_combine_kernel", "bound": "hbm",
                      "achieved": round(bytes5 / t5 / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(bytes5 / t5 / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(bytes5 / t5 / 1e9 / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_c5"),
                      "mfma_frac": round(flops5 / t5 / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
     del kv5, gc
