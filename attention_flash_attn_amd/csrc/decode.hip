@@ -269,10 +269,19 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
 // The selected rows of the token are gathered straight from the row cache in
 // their native layout (the approach of the "MLA Decode Attention Kernel API
 // Reference" page, Background: no pre-gathered copy), 32 rows per step, into
-// an LDS double buffer shared by the NW waves; each wave owns 16 heads (the
-// query columns of its 16x16x32 MFMAs) and the whole value width. When the
-// value is a prefix of the key row (v_cache == k_cache) the rows are loaded
-// once. A key is live iff its position is at or before the token's.
+// a ring of NST LDS stages shared by the NW waves (NST-1 steps in flight);
+// each wave owns 16 heads (the query columns of its 16x16x32 MFMAs) and the
+// whole value width. When the value is a prefix of the key row (VK) the rows
+// are loaded once and the value operand is read from the key stage. A key is
+// live iff its position is at or before the token's.
+//
+// Stage layout: 32 rows at a pitch of one row (DK*2 bytes, 128 mod 256), so
+// each 1 KB direct load reads contiguous global memory. Row r stores its
+// logical 16-byte chunk c at c ^ sw(r) (sw(r) < 8 permutes within aligned
+// groups of 8 chunks); with that swizzle both reads are conflict-free and
+// every address is one of a few per-lane bases plus an immediate:
+//   K operand: a 128-bit read of one chunk by 16 consecutive rows;
+//   V^T operand: a transposing read of 4 consecutive rows x 32 bytes.
 struct GatherParams {
     const uint16_t* __restrict__ q;
     const uint16_t* __restrict__ kc;
@@ -282,7 +291,7 @@ struct GatherParams {
     const int32_t* __restrict__ row_index;
     const float* __restrict__ key_pos;
     const int32_t* __restrict__ q_pos;
-    int T, Hq, n_sel, n_split, split_len, v_is_k;
+    int T, Hq, n_sel, n_split, split_len;
     long long row_stride;  // elements
     float c_score, c_tanh, c_cap;
     int causal, softcap_on;
@@ -290,21 +299,43 @@ struct GatherParams {
 
 constexpr int kGatherMaxSplit = 1024;  // keys per split the LDS index table holds
 
-template <int DK, int DV, int NW>
+#ifndef ATTN_GPF_K
+#define ATTN_GPF_K 4  // K fragments read ahead of their MFMA
+#endif
+#ifndef ATTN_GPF_V
+#define ATTN_GPF_V 4  // V^T fragments read ahead of their MFMA
+#endif
+
+// Wait until at most `later` stages of LPS direct loads per wave are still in flight.
+template <int LPS>
+__device__ __forceinline__ void wait_stages(int later) {
+    if (later >= 2)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
+    else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int DK, int DV, int NW, bool VK>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_gathered_split_kernel(GatherParams p) {
     constexpr int NT = NW * 64;
-    constexpr int KQ = DK / 32;          // QK k-steps of 32
-    constexpr int DBV = DV / 16;         // 16-row blocks of O^T
-    constexpr int KROW = DK * 2, VROW = DV * 2;
-    constexpr int NCK = DK / 8, NCV = DV / 8;
-    constexpr int KSTAGE = 32 * KROW, VSTAGE = 32 * VROW;
-    constexpr int KSEG = KSTAGE / 1024, VSEG = VSTAGE / 1024;
-    static_assert(DK % 32 == 0 && DV % 16 == 0 && KSTAGE % 1024 == 0 && VSTAGE % 1024 == 0, "shape");
-    __shared__ __attribute__((aligned(1024))) char kst[2 * KSTAGE];
-    __shared__ __attribute__((aligned(1024))) char vst[2 * VSTAGE];
+    constexpr int KQ = DK / 32;   // QK k-steps of 32 dims
+    constexpr int DBV = DV / 16;  // 16-column blocks of O^T
+    constexpr int PITCH = DK * 2;             // LDS row pitch (bytes), key and value stages alike
+    constexpr int NCH = DK / 8;               // 16-byte chunks per row
+    constexpr int SSTAGE = 32 * PITCH;        // one stage of 32 rows
+    constexpr int NSEG = SSTAGE / 1024;       // 1 KB direct loads per stage
+    constexpr int STAGE = SSTAGE * (VK ? 1 : 2);
+    constexpr int NST = VK ? 4 : 2;
+    constexpr int LPS = (NSEG / NW) * (VK ? 1 : 2);  // direct loads per wave per stage
+    static_assert(DK % 32 == 0 && DV % 64 == 0 && DV <= DK && PITCH % 128 == 0 && PITCH % 256 != 0, "shape");
+    static_assert(SSTAGE % 1024 == 0 && NSEG % NW == 0 && NCH % 8 == 0, "stage");
+    static_assert(NST * STAGE + 8 * kGatherMaxSplit <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
     __shared__ int32_t srow[kGatherMaxSplit];
-    __shared__ float spos[kGatherMaxSplit];
+    __shared__ __attribute__((aligned(16))) float spos[kGatherMaxSplit];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, c16 = lane & 15;
     const int split = blockIdx.x, hgrp = blockIdx.y, t = blockIdx.z;
@@ -313,17 +344,13 @@ void decode_gathered_split_kernel(GatherParams p) {
     const int nk = end - start;
     const float qpos = (float)p.q_pos[t];
 
-    // row indices and positions of this split, once; LDS starts finite
     for (int i = tid; i < nk; i += NT) {
         srow[i] = p.row_index[(size_t)t * p.n_sel + start + i];
         spos[i] = p.key_pos[(size_t)t * p.n_sel + start + i];
     }
-    for (int i = tid; i < 2 * KSTAGE / 16; i += NT) *(u32x4*)(kst + i * 16) = u32x4{0, 0, 0, 0};
-    if (!p.v_is_k)
-        for (int i = tid; i < 2 * VSTAGE / 16; i += NT) *(u32x4*)(vst + i * 16) = u32x4{0, 0, 0, 0};
     __syncthreads();
 
-    const int h = hgrp * (NW * 16) + wave * 16 + c16;  // this lane's head (query column)
+    const int h = hgrp * (NW * 16) + wave * 16 + c16;
     const bool hok = h < p.Hq;
     bf16x8 qf[KQ];
     {
@@ -336,34 +363,37 @@ void decode_gathered_split_kernel(GatherParams p) {
         }
     }
 
-    // rows of step i into stage st: every wave issues every NW-th 1 KB segment
+    // row r stores logical chunk c at chunk c ^ sw(r) (within aligned groups of 8)
+    auto sw = [](int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); };
+    // Rows of step i into stage st: wave w fills 1 KB segments w, w+NW, ...
     auto issue = [&](int i, int st) {
-        const int r0 = i * 32;
+        char* sb = smem + st * STAGE;
 #pragma unroll
-        for (int j = 0; j < (KSEG + NW - 1) / NW; ++j) {
-            const int s = wave + j * NW;
-            if (s < KSEG) {
-                const int off = s * 1024 + lane * 16;
-                const int r = off / KROW;
-                const int c = ((off % KROW) >> 4) ^ swz<NCK, true>(r);
-                const int kr = min(r0 + r, nk - 1);  // rows past the split repeat its last row (finite, masked)
-                load_lds16(p.kc + (size_t)srow[kr] * p.row_stride + c * 8, kst + st * KSTAGE + s * 1024);
-            }
-        }
-        if (!p.v_is_k) {
-#pragma unroll
-            for (int j = 0; j < (VSEG + NW - 1) / NW; ++j) {
-                const int s = wave + j * NW;
-                if (s < VSEG) {
-                    const int off = s * 1024 + lane * 16;
-                    const int r = off / VROW;
-                    const int c = ((off % VROW) >> 4) ^ swz<NCV, true>(r);
-                    const int kr = min(r0 + r, nk - 1);
-                    load_lds16(p.vc + (size_t)srow[kr] * p.row_stride + c * 8, vst + st * VSTAGE + s * 1024);
-                }
+        for (int j = 0; j < NSEG / NW; ++j) {
+            const int sg = wave + j * NW;
+            const int off = sg * 1024 + lane * 16;
+            const int r = off / PITCH;
+            const int c = ((off - r * PITCH) >> 4) ^ sw(r);
+            const int kr = min(i * 32 + r, nk - 1);
+            const size_t rb = (size_t)srow[kr] * (size_t)p.row_stride;
+            load_lds16(p.kc + rb + c * 8, sb + sg * 1024);
+            if constexpr (!VK) {
+                // value rows use the same layout; chunks past the value width repeat earlier ones
+                load_lds16(p.vc + rb + (c % (DV / 8)) * 8, sb + SSTAGE + sg * 1024);
             }
         }
     };
+
+    // per-lane LDS byte offsets within a stage
+    const int sk = sw(c16);  // rows c16 and c16 + 16
+    const int kofs0 = c16 * PITCH + ((grp ^ sk) << 4);        // even k-steps (+ kk/2 * 128)
+    const int kofs1 = c16 * PITCH + (((4 + grp) ^ sk) << 4);  // odd k-steps
+    const int ra = grp * 4 + (c16 >> 2);
+    const int sv = sw(ra);
+    const int xv = (c16 & 3) >> 1, bv = (c16 & 1) * 8;
+    int vofs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vofs[j] = ra * PITCH + (((2 * j + xv) ^ sv) << 4) + bv;
 
     f32x4 oacc[DBV];
 #pragma unroll
@@ -371,47 +401,61 @@ void decode_gathered_split_kernel(GatherParams p) {
     float m_run = -INFINITY, l_run = 0.f;
 
     const int nsteps = (nk + 31) / 32;
-    if (nsteps > 0) issue(0, 0);
+    for (int j = 0; j < NST - 1 && j < nsteps; ++j) issue(j, j);
+#pragma clang loop unroll(disable)
     for (int i = 0; i < nsteps; ++i) {
-        wait_vmem();
+        wait_stages<LPS>(min(NST - 2, nsteps - 1 - i));
         __syncthreads();
-        if (i + 1 < nsteps) issue(i + 1, (i + 1) & 1);
+        if (i + NST - 1 < nsteps) issue(i + NST - 1, (i + NST - 1) % NST);
         __builtin_amdgcn_sched_barrier(0);
-        const char* kt = kst + (i & 1) * KSTAGE;
-        const char* vt = p.v_is_k ? kt : vst + (i & 1) * VSTAGE;
-        const int vrow = p.v_is_k ? KROW : VROW;
+        const char* kt = smem + (i % NST) * STAGE;
+        const char* vt = VK ? kt : kt + SSTAGE;
         const int r0 = i * 32;
-
-        // S^T: two 16-key blocks; A = K rows (key c16 of the block), k-step kk
-        f32x4 sacc[2];
+        f32x4 kpos[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if (p.causal) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int r = kb * 16 + c16;
-            const char* krow = kt + r * KROW;
-#pragma unroll
-            for (int kk = 0; kk < KQ; ++kk) {
-                const int c = kk * 4 + grp;
-                const bf16x8 a = *(const bf16x8*)(krow + ((c ^ swz<NCK, true>(r)) * 16));
-                sacc[kb] = mfma16x16x32(a, qf[kk], sacc[kb]);
-            }
+            for (int kb = 0; kb < 2; ++kb) kpos[kb] = *(const f32x4*)(spos + r0 + kb * 16 + grp * 4);
         }
+
+        constexpr int NQK = 2 * KQ;
+        constexpr int PFK = NQK < ATTN_GPF_K ? NQK : ATTN_GPF_K;
+        auto kload = [&](int idx) -> bf16x8 {
+            const int kk = idx >> 1, kb = idx & 1;
+            const int o = ((kk & 1) ? kofs1 : kofs0) + (kk >> 1) * 128 + kb * 16 * PITCH;
+            return *(const bf16x8*)(kt + o);
+        };
+        f32x4 sacc[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb][0] = sacc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 kring[PFK];
+#pragma unroll
+        for (int j = 0; j < PFK; ++j) kring[j] = kload(j);
+#pragma unroll
+        for (int idx = 0; idx < NQK; ++idx) {
+            const bf16x8 a = kring[idx % PFK];
+            if (idx + PFK < NQK) kring[idx % PFK] = kload(idx + PFK);
+            const int kk = idx >> 1, kb = idx & 1;
+            sacc[kb][kk & 1] = mfma16x16x32(a, qf[kk], sacc[kb][kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        f32x4 sc[2];
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = sacc[kb][0] + sacc[kb][1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float x = sacc[kb][e];
+                float x = sc[kb][e];
                 if (p.softcap_on) {
                     const float ex = exp2_fast(x * p.c_tanh);
                     x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(ex + 1.f);
                 } else {
                     x *= p.c_score;
                 }
-                const int kl = r0 + kb * 16 + grp * 4 + e;  // key within the split
-                const bool live = kl < nk && (!p.causal || spos[kl] <= qpos);
+                const int kl = r0 + kb * 16 + grp * 4 + e;
+                const bool live = kl < nk && (!p.causal || kpos[kb][e] <= qpos);
                 if (!live) x = -INFINITY;
-                sacc[kb][e] = x;
+                sc[kb][e] = x;
                 mx = fmaxf(mx, x);
             }
         }
@@ -428,24 +472,29 @@ void decode_gathered_split_kernel(GatherParams p) {
         uint32_t pk[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            pk[2 * kb] = pack_bf16x2(exp2_fast(sacc[kb][0] + nm), exp2_fast(sacc[kb][1] + nm));
-            pk[2 * kb + 1] = pack_bf16x2(exp2_fast(sacc[kb][2] + nm), exp2_fast(sacc[kb][3] + nm));
+            pk[2 * kb] = pack_bf16x2(exp2_fast(sc[kb][0] + nm), exp2_fast(sc[kb][1] + nm));
+            pk[2 * kb + 1] = pack_bf16x2(exp2_fast(sc[kb][2] + nm), exp2_fast(sc[kb][3] + nm));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) l_run = add_bf16x2(pk[j], l_run);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-        const int ra = grp * 4 + (c16 >> 2);
-        const int rb = ra + 16;
-        const int swzv = p.v_is_k ? 0 : 1;  // row swizzle of the V rows' stage
+
+        constexpr int PFV = DBV < ATTN_GPF_V ? DBV : ATTN_GPF_V;
+        auto vload = [&](int d) -> bf16x8 {
+            const char* pa = vt + vofs[d & 3] + (d >> 2) * 128;
+            const bf16x4 va = lds_read_tr16(pa);
+            const bf16x4 vb = lds_read_tr16(pa + 16 * PITCH);  // rows + 16
+            return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 vring[PFV];
+#pragma unroll
+        for (int j = 0; j < PFV; ++j) vring[j] = vload(j);
 #pragma unroll
         for (int d = 0; d < DBV; ++d) {
-            const int dc = d * 16 + (c16 & 3) * 4;
-            const int ch = dc >> 3, within = (dc & 7) * 2;
-            const int cha = swzv ? (ch ^ swz<NCV, true>(ra)) : (ch ^ swz<NCK, true>(ra));
-            const int chb = swzv ? (ch ^ swz<NCV, true>(rb)) : (ch ^ swz<NCK, true>(rb));
-            const bf16x4 va = lds_read_tr16(vt + ra * vrow + cha * 16 + within);
-            const bf16x4 vb = lds_read_tr16(vt + rb * vrow + chb * 16 + within);
-            oacc[d] = mfma16x16x32(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[d]);
+            const bf16x8 a = vring[d % PFV];
+            if (d + PFV < DBV) vring[d % PFV] = vload(d + PFV);
+            oacc[d] = mfma16x16x32(a, pb, oacc[d]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -472,9 +521,13 @@ struct CombineParams {
     int Sq, Hq, n_split, split_len, dv;
 };
 
-// One wavefront per output row (b, query, head).
+// One wavefront per output row (b, query, head). Each lane owns 4 columns; the
+// splits are read 8 at a time (indices clamped, weights of missing splits 0) so
+// that many loads are in flight. Rows narrower than 256 columns put the spare
+// lanes on other splits and add the phases up in LDS.
 template <bool OF32>
 __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
+    constexpr int U = 8;
     const int lane = threadIdx.x;
     const size_t row = blockIdx.x;
     const int h = (int)(row % p.Hq);
@@ -500,17 +553,49 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
     if (has_sink) l += exp2_fast(sink2 - Mu);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float* ob = p.ws_o + row * p.n_split * p.dv;
-    for (int d = lane * 4; d < p.dv; d += 256) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < nv; ++s) {
-            const float w = exp2_fast(ml[2 * s] - Mu);
-            if (w != 0.f) acc += w * *(const f32x4*)(ob + (size_t)s * p.dv + d);
-        }
+    const int ncg = p.dv >> 2;  // 4-column groups
+
+    auto store = [&](int c, f32x4 acc) {
         acc *= inv;
         if constexpr (OF32) {
-            *(f32x4*)((float*)p.o + row * p.dv + d) = acc;
+            *(f32x4*)((float*)p.o + row * p.dv + c * 4) = acc;
         } else {
-            *(u32x2*)((uint16_t*)p.o + row * p.dv + d) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *(u32x2*)((uint16_t*)p.o + row * p.dv + c * 4) =
+                u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        }
+    };
+    // sum over splits s = s_first, s_first + stride, ... (< nv) of w_s * O_s[columns 4c..4c+3]
+    auto accumulate = [&](int c, int s_first, int stride) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = s_first; s0 < nv; s0 += U * stride) {
+            f32x4 x[U];
+            float w[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int s = s0 + u * stride;
+                const int sc = min(s, nv - 1);
+                w[u] = s < nv ? exp2_fast(ml[2 * sc] - Mu) : 0.f;
+                x[u] = *(const f32x4*)(ob + (size_t)sc * p.dv + c * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc += w[u] * x[u];
+        }
+        return acc;
+    };
+
+    if (ncg >= 64) {
+        for (int c = lane; c < ncg; c += 64) store(c, accumulate(c, 0, 1));
+    } else {
+        __shared__ f32x4 red[64];
+        const int G = 64 / ncg;  // split phases
+        const int c = lane % ncg, ph = lane / ncg;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (ph < G) acc = accumulate(c, ph, G);
+        red[lane] = acc;
+        __syncthreads();
+        if (ph == 0) {
+            for (int g = 1; g < G; ++g) acc += red[g * ncg + c];
+            store(c, acc);
         }
     }
 }
@@ -617,7 +702,6 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         gp.n_sel = a.n_sel;
         gp.n_split = pl.n_split;
         gp.split_len = pl.split_len;
-        gp.v_is_k = a.v_cache == a.k_cache;
         gp.row_stride = a.row_stride;
         gp.c_score = sp.c_score;
         gp.c_tanh = sp.c_tanh;
@@ -626,7 +710,10 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         gp.softcap_on = sp.softcap_on;
         constexpr int NW = 4;
         const dim3 ggrid((unsigned)pl.n_split, (unsigned)((a.Hq + NW * 16 - 1) / (NW * 16)), (unsigned)a.B);
-        hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW>), ggrid, dim3(NW * 64), 0, stream, gp);
+        if (a.v_cache == a.k_cache)
+            hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, true>), ggrid, dim3(NW * 64), 0, stream, gp);
+        else
+            hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, false>), ggrid, dim3(NW * 64), 0, stream, gp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_combine(a, pl, ws_o, ws_ml, nullptr, stream);
