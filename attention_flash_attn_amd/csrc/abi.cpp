@@ -140,6 +140,9 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
         return fail(ATTN_ERR_UNSUPPORTED, "%s decode (dk, dv) = (%d, %d) is not built", gathered ? "gathered" : "paged",
                     dk, dv);
     const attn::DecodePlan pl = attn::decode_plan(B, Hq, Hkv, Sq, Sk_max, dk, dv);
+    if (B > 65535 || pl.n_split > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large (B = %d, %d key splits; at most 65535 each)", B,
+                    pl.n_split);
     if (!workspace || workspace_bytes < pl.ws_bytes)
         return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", pl.ws_bytes, workspace_bytes);
     if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");

@@ -58,7 +58,9 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
     __shared__ __attribute__((aligned(1024))) char vl[2 * STAGE];
 
     const int lane = threadIdx.x, grp = lane >> 4, c16 = lane & 15;
-    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // split-major grid: every (KV head, sequence) pair of split 0 first, then split 1, ...,
+    // so the last work dispatched belongs to the longest sequences' final (often partial) splits
+    const int split = blockIdx.z, g = blockIdx.x, b = blockIdx.y;
     const int L = p.seq_lens[b];
     const int start = split * p.split_len;
     if (start >= L) return;  // the combine pass only reads splits that start below L
@@ -643,11 +645,22 @@ bool decode_supported(int dk, int dv, bool gathered) {
 }
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv) {
-    (void)Hkv;
-    (void)dk;
     DecodePlan pl;
-    // keys per split: long caches get long splits (fewer partial rows to merge)
-    pl.split_len = Sk_max >= 16384 ? 1024 : Sk_max >= 4096 ? 512 : 256;
+    if (dk == 576 && dv == 512) {
+        // gathered rows: one split per 8 MFMA steps of the 64-head workgroups up to 2048
+        // selected keys, longer splits beyond (at most the LDS index table of a split)
+        pl.split_len = Sk_max >= 16384 ? 1024 : Sk_max >= 4096 ? 512 : 256;
+    } else {
+        // paged: one wavefront per (split, KV head, sequence). Aim for about 4096 of them
+        // (two rounds of two waves per SIMD) with splits of 256..2048 keys: long splits
+        // when there are many sequences (fewer partial rows to merge), short ones when few
+        const long long pairs = (long long)B * Hkv;
+        const long long want = (4096 + pairs - 1) / pairs;  // splits per (KV head, sequence)
+        long long len = Sk_max > 0 ? (Sk_max + want - 1) / want : 256;
+        int sl = 256;
+        while (sl < len && sl < 2048) sl <<= 1;
+        pl.split_len = sl;
+    }
     pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;
     pl.n_rows = B * Sq * Hq;
     pl.ws_bytes = (size_t)pl.n_rows * pl.n_split * ((size_t)dv + 2) * sizeof(float);
@@ -718,7 +731,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         if (e != hipSuccess) return e;
         return launch_combine(a, pl, ws_o, ws_ml, nullptr, stream);
     }
-    const dim3 grid((unsigned)pl.n_split, (unsigned)a.Hkv, (unsigned)a.B);
+    const dim3 grid((unsigned)a.Hkv, (unsigned)a.B, (unsigned)pl.n_split);
     switch (a.dk * 1000 + a.dv) {
         case 16016: e = launch_paged<16, 16>(sp, grid, stream); break;
         case 32032: e = launch_paged<32, 32>(sp, grid, stream); break;

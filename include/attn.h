@@ -105,7 +105,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
 /*
  * Decode attention: Sq query rows per sequence (Sq = 1 is the single-token
  * case) against a KV cache read in one of two modes. The keys are split into
- * fixed-size ranges processed in parallel, then merged by log-sum-exp.
+ * fixed-size ranges processed in parallel, then merged by log-sum-exp. The
+ * range length (256..2048 keys) depends only on the sizes passed here and to
+ * attn_decode_workspace_bytes; B and the number of ranges must not exceed
+ * 65535 (ATTN_ERR_UNSUPPORTED otherwise).
  *
  *   q   bf16 [B, Sq, Hq, dk] contiguous;   o [B, Sq, Hq, dv] of type o_dtype.
  *

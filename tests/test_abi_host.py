@@ -107,9 +107,13 @@ def test_decode_rejects(kw, status):
 
 
 def test_workspace_bytes():
-    # 32768 keys use 1024-key splits: 32 splits, (dv + 2) floats per row per split
+    # paged, 64 sequences x 8 KV heads: 2048-key splits (16 splits of 32768 keys),
+    # (dv + 2) floats per row per split
     n = attn.attn_decode_workspace_bytes(64, 64, 8, 1, 32768, 128, 128)
-    assert n >= 64 * 64 * 32 * 130 * 4
+    assert n >= 64 * 64 * 16 * 130 * 4
+    # one sequence: 256-key splits keep about 4096 wavefronts busy
+    n = attn.attn_decode_workspace_bytes(1, 8, 8, 1, 16384, 128, 128)
+    assert n >= 1 * 8 * 64 * 130 * 4
     # 2048 keys use 256-key splits: 8 splits
     n = attn.attn_decode_workspace_bytes(16, 128, 1, 1, 2048, 576, 512)
     assert n >= 16 * 128 * 8 * 514 * 4
