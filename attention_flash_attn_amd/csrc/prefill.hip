@@ -69,10 +69,10 @@ constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
 // Tile configurations (keys per tile, waves per workgroup, target waves per SIMD)
 #ifndef ATTN_D128_CFG
-#define ATTN_D128_CFG 64, 4, 2
+#define ATTN_D128_CFG 64, 8, 2
 #endif
 #ifndef ATTN_D256_CFG
-#define ATTN_D256_CFG 64, 4, 1
+#define ATTN_D256_CFG 32, 8, 2
 #endif
 
 template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool OF32>

@@ -73,7 +73,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-other", action="store_true", help="skip the extra workloads")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) pairs in the CPU sample")
@@ -289,9 +289,9 @@ def main():
             def run(q=q, k=k, v=v, o=o, sk=sk, c=c):
                 binding.attn_prefill_fwd(q, k, v, o, None, scale=c["scale"], causal=c["causal"],
                                          softcap=c["softcap"], sinks=sk)
-            for _ in range(2):
+            for _ in range(20):  # steady clocks before timing
                 run()
-            reps = 10
+            reps = 20
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
