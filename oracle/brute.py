@@ -30,9 +30,11 @@ def _tanh(y):
     return (e2 - 1) / (e2 + 1)
 
 
-def attention_rows_decimal(qrows, keys, values, scale, softcap=0.0, sink=None, visible=None):
+def attention_rows_decimal(qrows, keys, values, scale, softcap=0.0, sink=None, visible=None, add=None):
     """qrows: list of R lists (dk); keys: list of N lists (dk); values: list of N lists (dv).
-    visible(r, j) -> bool or None. Returns (o as list of lists of Decimal, lse list)."""
+    visible(r, j) -> bool or None; add(r, j) -> float (an additive score term applied
+    after the softcap; -inf hides the key) or None. Returns (o as list of lists of
+    Decimal, lse list)."""
     sc = _d(scale)
     cap = _d(softcap)
     outs, lses = [], []
@@ -47,6 +49,11 @@ def attention_rows_decimal(qrows, keys, values, scale, softcap=0.0, sink=None, v
             s = s * sc
             if cap != 0:
                 s = cap * _tanh(s / cap)
+            if add is not None:
+                extra = float(add(r, j))
+                if extra == float("-inf"):
+                    continue
+                s = s + _d(extra)
             terms.append((s, values[j]))
         n_live = len(terms)
         if sink is not None:
@@ -73,8 +80,10 @@ def attention_rows_decimal(qrows, keys, values, scale, softcap=0.0, sink=None, v
     return outs, lses
 
 
-def prefill_decimal(q, k, v, scale, causal=False, softcap=0.0, sinks=None):
+def prefill_decimal(q, k, v, scale, causal=False, softcap=0.0, sinks=None, mask=None, slopes=None):
     """q [B][Sq][Hq][dk], k [B][Sk][Hkv][dk], v [B][Sk][Hkv][dv] as nested lists of floats.
+    mask [MB][MH][Sq][Sk] (nested lists, may hold -inf) is added to head h of batch b
+    as slopes[h] * mask[b % MB][h % MH] (slopes given explicitly; 1 when None).
     Returns o [B][Sq][Hq][dv] and lse [B][Hq][Sq] (None for -inf), all Decimal."""
     B, Sq, Hq = len(q), len(q[0]), len(q[0][0])
     Sk, Hkv = len(k[0]), len(k[0][0])
@@ -92,7 +101,13 @@ def prefill_decimal(q, k, v, scale, causal=False, softcap=0.0, sinks=None):
                 off = Sk - Sq
                 vis = (lambda r, j, off=off: j <= r + off)
             sink = None if sinks is None else sinks[h]
-            ob, lb = attention_rows_decimal(qrows, keys, vals, scale, softcap, sink, vis)
+            add = None
+            if mask is not None:
+                mrow = mask[b % len(mask)][h % len(mask[0])]
+                sl = 1.0 if slopes is None else slopes[h]
+                add = (lambda r, j, mrow=mrow, sl=sl:
+                       float("-inf") if mrow[r][j] == float("-inf") else sl * mrow[r][j])
+            ob, lb = attention_rows_decimal(qrows, keys, vals, scale, softcap, sink, vis, add)
             for i in range(Sq):
                 o[b][i][h] = ob[i]
                 lse[b][h][i] = lb[i]

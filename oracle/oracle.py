@@ -10,7 +10,8 @@ score matrix at a time, with no tiling and no online softmax:
 
     x_j = scale * <q, k_j>                          raw dot product, then scale
     x_j = softcap * tanh(x_j / softcap)             only when softcap != 0
-    keys that the mask excludes are dropped
+    x_j = x_j + slope_h * mask[i, j]                only with an additive mask
+    keys that the mask excludes (causal, position, length, mask = -inf) are dropped
     m   = max over the live x_j and the head's sink logit (when sinks are given)
     Z   = sum_j exp(x_j - m) + exp(sink - m)
     o   = sum_j exp(x_j - m) * v_j / Z              (0 when no key is live)
@@ -38,12 +39,19 @@ Readings where the pages are silent (each listed in the design notes):
   * a sink is a raw fp32 logit per query head: not scaled, not softcapped.
   * a row with no live key and no sink gives o = 0 and lse = -inf; with a sink
     but no live key it gives o = 0 (the sink carries no value).
+  * ALiBi: the page passes m0, m1 and n_head_log2 to the kernel and takes the
+    slope of head h as m0^(h+1) for h < n_head_log2, else m1^(2(h-n_head_log2)+1);
+    how the host derives them is off the page. The reading taken is the ALiBi
+    schedule that this exponent pattern produces: n_head_log2 the largest power
+    of two <= Hq, m0 = 2^(-max_bias / n_head_log2), m1 = 2^(-max_bias / (2 n_head_log2)).
+    max_bias = 0 gives slope 1 (the mask is added as is).
 """
 
 import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64",
+    "alibi_slopes",
     "attend_rows",
     "prefill",
     "decode_paged",
@@ -66,16 +74,32 @@ def _as_f64(a):
     return a.astype(np.float64)
 
 
-def attend_rows(qrows, keys, values, scale, softcap=0.0, sink=None, live=None):
+def alibi_slopes(n_heads, max_bias):
+    """Per-head ALiBi slope (float64 [n_heads]); the "ggml-metal: FA tensor path"
+    page, fa.metal tensor kernel: base m0 for the first n_head_log2 heads with
+    exponent h + 1, base m1 for the rest with exponent 2 (h - n_head_log2) + 1."""
+    if max_bias == 0.0:
+        return np.ones(n_heads)
+    n_log2 = 1
+    while n_log2 * 2 <= n_heads:
+        n_log2 *= 2
+    m0 = 2.0 ** (-max_bias / n_log2)
+    m1 = 2.0 ** (-max_bias / 2.0 / n_log2)
+    h = np.arange(n_heads)
+    return np.where(h < n_log2, m0 ** (h + 1), m1 ** (2 * (h - n_log2) + 1))
+
+
+def attend_rows(qrows, keys, values, scale, softcap=0.0, sink=None, live=None, bias=None):
     """Attention of a block of query rows against one key/value set.
 
     qrows [R, dk], keys [N, dk], values [N, dv]; live [R, N] boolean (True =
-    key visible to that row) or None for all visible; sink is a scalar logit or
-    None. Returns (o [R, dv], lse [R]) in float64.
+    key visible to that row) or None for all visible; bias [R, N] an additive
+    term (already multiplied by the head's slope; -inf drops the key) or None;
+    sink is a scalar logit or None. Returns (o [R, dv], lse [R]) in float64.
 
     Follows the tensor kernel on the "ggml-metal: FA tensor path" page: raw
-    product, scale, softcap, mask, softmax with the sink as an extra term of the
-    normaliser, division by the sum with the empty-row rule.
+    product, scale, softcap, additive mask, softmax with the sink as an extra
+    term of the normaliser, division by the sum with the empty-row rule.
     """
     qrows = np.asarray(qrows, dtype=np.float64)
     keys = np.asarray(keys, dtype=np.float64)
@@ -88,6 +112,10 @@ def attend_rows(qrows, keys, values, scale, softcap=0.0, sink=None, live=None):
         x = softcap * np.tanh(x / softcap)
     if live is None:
         live = np.ones((R, N), dtype=bool)
+    if bias is not None:
+        bias = np.asarray(bias, dtype=np.float64)
+        live = live & (bias > -np.inf)              # a -inf mask entry drops the key
+        x = x + np.where(live, bias, 0.0)           # added after the softcap
     x = np.where(live, x, -np.inf)                  # excluded keys drop out
 
     m = x.max(axis=1) if N > 0 else np.full(R, -np.inf)
@@ -115,12 +143,15 @@ def _causal_live(q_positions, Nk):
 
 
 def prefill(q, k, v, scale, causal=False, softcap=0.0, sinks=None,
-            rows=None, heads=None, batches=None):
+            rows=None, heads=None, batches=None, mask=None, max_bias=0.0):
     """Dense prefill attention.
 
     q [B, Sq, Hq, dk], k [B, Sk, Hkv, dk], v [B, Sk, Hkv, dv] (uint16 bf16 bits
     or floats); sinks [Hq] or None. Query head h reads KV head h // (Hq // Hkv)
     (contiguous groups). Causal is bottom-right aligned.
+    mask [MB, MH, Sq, >= Sk] (float16 or float; extra columns ignored) is added
+    to the scores of batch b, head h from mask[b % MB, h % MH] (the broadcast of
+    the page's kernel), times the head's ALiBi slope for max_bias.
 
     rows / heads / batches optionally restrict the work to a subset (for
     sampled checks at large sizes); the returned arrays then hold only those
@@ -141,12 +172,19 @@ def prefill(q, k, v, scale, causal=False, softcap=0.0, sinks=None,
     o = np.zeros((len(batches), len(rows), len(heads), dv))
     lse = np.zeros((len(batches), len(heads), len(rows)))
     live = _causal_live(rows + (Sk - Sq), Sk) if causal else None
+    if mask is not None:
+        mask = np.asarray(mask)
+        slopes = alibi_slopes(Hq, max_bias)
     for bi, b in enumerate(batches):
         for hi, h in enumerate(heads):
             g = h // group
             sink = None if sinks is None else float(np.asarray(sinks, dtype=np.float64)[h])
+            bias = None
+            if mask is not None:
+                mrows = mask[b % mask.shape[0], h % mask.shape[1]][rows][:, :Sk].astype(np.float64)
+                bias = slopes[h] * mrows
             ob, lb = attend_rows(q[b, rows, h, :], k[b, :, g, :], v[b, :, g, :],
-                                 scale, softcap, sink, live)
+                                 scale, softcap, sink, live, bias)
             o[bi, :, hi, :] = ob
             lse[bi, hi, :] = lb
     return o, lse

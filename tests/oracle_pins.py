@@ -332,4 +332,100 @@ def pin_gathered(orc):
     _close(o, o2, 1e-13, "selection order")
 
 
+# ---------------------------------------------------------------- additive mask, ALiBi
+def pin_alibi_slopes_published(orc):
+    """The ALiBi slope schedule (Press, Smith and Lewis, "Train Short, Test Long"):
+    n heads (a power of two) get 2^(-8/n), 2^(-16/n), ..., 2^(-8) for a maximum bias
+    of 8; other head counts take the slopes of the nearest smaller power of two,
+    then every other slope of twice that count. Written out by hand below."""
+    _close(orc.alibi_slopes(8, 8.0), [2.0 ** -e for e in range(1, 9)], 1e-15, "8-head slopes")
+    table12 = [2.0 ** -e for e in range(1, 9)] + [2.0 ** -0.5, 2.0 ** -1.5, 2.0 ** -2.5, 2.0 ** -3.5]
+    _close(orc.alibi_slopes(12, 8.0), table12, 1e-15, "12-head slopes")
+    _close(orc.alibi_slopes(2, 8.0), [2.0 ** -4, 2.0 ** -8], 1e-15, "2-head slopes")
+    _close(orc.alibi_slopes(5, 0.0), np.ones(5), 0.0, "max_bias 0 leaves the mask unscaled")
+
+
+def _mask(rng, MB, MH, Sq, Sk, p_neg_inf=0.15):
+    m = _rand(rng, MB, MH, Sq, Sk, std=2.0)
+    m[rng.random(m.shape) < p_neg_inf] = -np.inf
+    return m
+
+
+def _brute_mask_compare(orc, B, Sq, Sk, Hq, Hkv, d, MB, MH, softcap, causal, max_bias, slopes, seed):
+    rng = _rng(seed)
+    q = _rand(rng, B, Sq, Hq, d)
+    k = _rand(rng, B, Sk, Hkv, d)
+    v = _rand(rng, B, Sk, Hkv, d)
+    mask = _mask(rng, MB, MH, Sq, Sk)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = orc.prefill(q, k, v, scale, causal=causal, softcap=softcap, mask=mask, max_bias=max_bias)
+    ob, lb = brute.prefill_decimal(q.tolist(), k.tolist(), v.tolist(), scale, causal, softcap,
+                                   None, mask.tolist(), slopes)
+    ob = np.array([[[[float(x) for x in row] for row in hh] for hh in ii] for ii in ob])
+    lb = np.array([[[(-math.inf if x is None else float(x)) for x in r] for r in hh] for hh in lb])
+    _close(o, ob, 1e-12, "masked o vs decimal brute force")
+    fin = np.isfinite(lb)
+    assert np.array_equal(fin, np.isfinite(lse)), "masked lse -inf pattern differs from brute force"
+    _close(lse[fin], lb[fin], 1e-12, "masked lse vs decimal brute force")
+
+
+def pin_brute_mask_alibi(orc):
+    """Additive mask after the softcap, per-head mask, ALiBi slopes of a 2-head model
+    (2^-4, 2^-8 for a maximum bias of 8), GQA, causal on top."""
+    _brute_mask_compare(orc, 1, 4, 6, 2, 1, 3, 1, 2, 1.5, True, 8.0, [2.0 ** -4, 2.0 ** -8], 61)
+
+
+def pin_brute_mask_broadcast(orc):
+    """One mask shared by both batches (MB = 1) and by both heads (MH = 1)."""
+    _brute_mask_compare(orc, 2, 3, 5, 2, 2, 4, 1, 1, 0.0, False, 0.0, None, 62)
+    _brute_mask_compare(orc, 2, 3, 5, 2, 2, 4, 2, 1, 0.0, False, 0.0, None, 63)
+
+
+def pin_mask_as_causal(orc):
+    """A mask of 0 on and below the bottom-right diagonal and -inf above it is the causal mask."""
+    rng = _rng(64)
+    B, Sq, Sk = 2, 5, 9
+    q = _rand(rng, B, Sq, 2, 4)
+    k = _rand(rng, B, Sk, 2, 4)
+    v = _rand(rng, B, Sk, 2, 3)
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    mask = np.where(j <= i + (Sk - Sq), 0.0, -np.inf)[None, None]
+    o1, l1 = orc.prefill(q, k, v, 0.4, causal=True)
+    o2, l2 = orc.prefill(q, k, v, 0.4, mask=mask)
+    _close(o1, o2, 1e-14, "causal as a mask")
+    _close(l1, l2, 1e-14, "lse of causal as a mask")
+
+
+def pin_mask_constant_shift(orc):
+    """Adding c to every mask entry shifts every score of head h by slope_h * c: the
+    output is unchanged and lse moves by slope_h * c (softmax shift invariance)."""
+    rng = _rng(65)
+    Hq = 4
+    q = _rand(rng, 1, 3, Hq, 4)
+    k = _rand(rng, 1, 6, 2, 4)
+    v = _rand(rng, 1, 6, 2, 5)
+    mask = _rand(rng, 1, Hq, 3, 6)
+    c = 1.75
+    slopes = [2.0 ** -2, 2.0 ** -4, 2.0 ** -6, 2.0 ** -8]   # 4 heads, maximum bias 8
+    o1, l1 = orc.prefill(q, k, v, 0.5, mask=mask, max_bias=8.0)
+    o2, l2 = orc.prefill(q, k, v, 0.5, mask=mask + c, max_bias=8.0)
+    _close(o1, o2, 1e-13, "output under a constant mask shift")
+    _close(l2 - l1, np.broadcast_to(np.array(slopes)[None, :, None] * c, l1.shape), 1e-13, "lse shift")
+
+
+def pin_mask_all_neg_inf(orc):
+    """A query row whose mask is -inf everywhere sees no key: o = 0 and lse = -inf."""
+    rng = _rng(66)
+    q = _rand(rng, 1, 3, 1, 4)
+    k = _rand(rng, 1, 5, 1, 4)
+    v = _rand(rng, 1, 5, 1, 3)
+    mask = np.zeros((1, 1, 3, 5))
+    mask[0, 0, 1, :] = -np.inf
+    o, lse = orc.prefill(q, k, v, 0.5, mask=mask)
+    assert np.array_equal(o[0, 1, 0], np.zeros(3)), "fully masked row must be 0"
+    assert lse[0, 0, 1] == -np.inf, "fully masked row has lse -inf"
+    assert np.isfinite(lse[0, 0, [0, 2]]).all()
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}

@@ -31,6 +31,14 @@ MUTATIONS = {
     "gathered_strict_position": ("(key_pos[t] <= float(q_pos[t]))", "(key_pos[t] < float(q_pos[t]))"),
     "gathered_value_rows": ("V = _as_f64(v_rows[r])", "V = _as_f64(v_rows[np.sort(r)])"),
     "max_ignores_mask": ("x = np.where(live, x, -np.inf)", "x = np.where(live, x, -1e3)"),
+    "mask_before_softcap": ("    if softcap != 0.0:\n        x = softcap * np.tanh(x / softcap)\n    if live is None:",
+                            "    if bias is not None:\n        x = x + np.where(np.asarray(bias) > -np.inf, bias, 0.0)\n"
+                            "    if softcap != 0.0:\n        x = softcap * np.tanh(x / softcap)\n    if live is None:"),
+    "mask_sign": ("x = x + np.where(live, bias, 0.0)", "x = x - np.where(live, bias, 0.0)"),
+    "mask_head_by_kv_group": ("mask[b % mask.shape[0], h % mask.shape[1]]", "mask[b % mask.shape[0], g % mask.shape[1]]"),
+    "alibi_exponent_off_by_one": ("m0 ** (h + 1)", "m0 ** h"),
+    "alibi_m1_base": ("m1 = 2.0 ** (-max_bias / 2.0 / n_log2)", "m1 = 2.0 ** (-max_bias / n_log2)"),
+    "alibi_slope_ignored": ("bias = slopes[h] * mrows", "bias = mrows"),
 }
 
 
