@@ -56,6 +56,11 @@ def load_library():
         lib.attn_prefill_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          c_float, c_int, c_float, c_void_p, c_void_p]
+        lib.attn_prefill_fwd_masked.restype = c_int
+        lib.attn_prefill_fwd_masked.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
+                                                c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                                c_float, c_int, c_float, c_void_p,
+                                                c_void_p, c_int, c_int, ctypes.c_int64, c_float, c_void_p]
         lib.attn_decode_workspace_bytes.restype = c_size_t
         lib.attn_decode_workspace_bytes.argtypes = [c_int] * 7
         lib.attn_decode_fwd.restype = c_int
@@ -142,6 +147,28 @@ def attn_prefill_fwd(q, k, v, o, lse=None, *, scale, causal=False, softcap=0.0, 
                               _ptr(lse, "lse", torch.float32, True),
                               B, Hq, Hkv, Sq, Sk, dk, dv, float(scale), int(bool(causal)), float(softcap),
                               _ptr(sinks, "sinks", torch.float32, True), _stream(stream))
+    _check(st)
+
+
+def attn_prefill_fwd_masked(q, k, v, o, mask, lse=None, *, scale, causal=False, softcap=0.0, sinks=None,
+                            max_bias=0.0, stream=None):
+    """attn_prefill_fwd plus an additive fp16 mask [MB, MH, Sq, W] (contiguous, W >= Sk and a
+    multiple of 4; entry [b % MB, h % MH] applies to batch b, head h) times the head's ALiBi
+    slope for max_bias."""
+    import torch
+    lib = load_library()
+    B, Sq, Hq, dk = q.shape
+    _, Sk, Hkv, _ = k.shape
+    dv = v.shape[3]
+    if mask.dim() != 4 or mask.shape[2] != Sq:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "mask must be [MB, MH, Sq, W] (got %s)" % (tuple(mask.shape),))
+    st = lib.attn_prefill_fwd_masked(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
+                                     _ptr(v, "v", torch.bfloat16), _ptr(o, "o"), _odtype(o),
+                                     _ptr(lse, "lse", torch.float32, True),
+                                     B, Hq, Hkv, Sq, Sk, dk, dv, float(scale), int(bool(causal)), float(softcap),
+                                     _ptr(sinks, "sinks", torch.float32, True),
+                                     _ptr(mask, "mask", torch.float16), int(mask.shape[0]), int(mask.shape[1]),
+                                     int(mask.shape[3]), float(max_bias), _stream(stream))
     _check(st)
 
 

@@ -62,20 +62,35 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
-attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
-                             int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale, int causal,
-                             float softcap, const float* sinks, void* stream) {
+static attn_status prefill_impl(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale, int causal,
+                                float softcap, const float* sinks, const void* mask, int mask_batch,
+                                int mask_heads, int64_t mask_row_stride, float max_bias, void* stream) {
     if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o are required");
     attn_status st = check_common(B, Hq, Hkv, Sq, dk, dv, scale, softcap, o_dtype);
     if (st != ATTN_OK) return st;
     if (Sk <= 0) return fail(ATTN_ERR_INVALID_ARG, "Sk must be positive (got %d)", Sk);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+    if (mask != nullptr) {
+        if (mask_batch <= 0 || mask_heads <= 0)
+            return fail(ATTN_ERR_INVALID_ARG, "mask_batch and mask_heads must be positive");
+        if (mask_row_stride < Sk || mask_row_stride % 4 != 0)
+            return fail(ATTN_ERR_INVALID_ARG, "mask_row_stride must be >= Sk and a multiple of 4 (got %lld)",
+                        (long long)mask_row_stride);
+        if (!aligned16(mask)) return fail(ATTN_ERR_INVALID_ARG, "mask must be 16-byte aligned");
+        if ((double)Sq * (double)mask_row_stride * 2.0 >= 4294967296.0)
+            return fail(ATTN_ERR_UNSUPPORTED, "one (batch, head) mask slab must be under 4 GiB");
+    }
+    if (!(std::isfinite(max_bias) && max_bias >= 0.f))
+        return fail(ATTN_ERR_INVALID_ARG, "max_bias must be finite and >= 0");
     if (!attn::prefill_supported(dk, dv))
         return fail(ATTN_ERR_UNSUPPORTED, "prefill (dk, dv) = (%d, %d) is not built", dk, dv);
     const double rows = (double)B * Sq * Hq;
     if ((double)B * ((Sq + 127) / 128) * Hq > 2147483647.0 || rows * dv > 9.0e18)
         return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    if ((double)Sk * Hkv * (dk > dv ? dk : dv) * 2.0 >= 4294967296.0)
+        return fail(ATTN_ERR_UNSUPPORTED, "K or V of one batch entry must be under 4 GiB");
 
     attn::PrefillArgs a;
     a.q = q;
@@ -95,9 +110,30 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* 
     a.scale = scale;
     a.causal = causal ? 1 : 0;
     a.softcap = softcap;
+    a.mask = mask;
+    a.mask_stride = (long long)mask_row_stride;
+    a.mask_batch = mask ? mask_batch : 1;
+    a.mask_heads = mask ? mask_heads : 1;
+    a.max_bias = max_bias;
     hipError_t e = attn::launch_prefill(a, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+                             int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale, int causal,
+                             float softcap, const float* sinks, void* stream) {
+    return prefill_impl(q, k, v, o, o_dtype, lse, B, Hq, Hkv, Sq, Sk, dk, dv, scale, causal, softcap, sinks,
+                        nullptr, 1, 1, 0, 0.f, stream);
+}
+
+attn_status attn_prefill_fwd_masked(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
+                                    int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale,
+                                    int causal, float softcap, const float* sinks, const void* mask,
+                                    int mask_batch, int mask_heads, int64_t mask_row_stride, float max_bias,
+                                    void* stream) {
+    return prefill_impl(q, k, v, o, o_dtype, lse, B, Hq, Hkv, Sq, Sk, dk, dv, scale, causal, softcap, sinks, mask,
+                        mask_batch, mask_heads, mask_row_stride, max_bias, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv) {

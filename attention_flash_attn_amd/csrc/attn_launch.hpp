@@ -19,6 +19,11 @@ struct PrefillArgs {
     float scale;
     int causal;
     float softcap;
+    // additive fp16 mask [mask_batch, mask_heads, Sq, mask_stride] (NULL: none) and ALiBi
+    const void* mask = nullptr;
+    long long mask_stride = 0;
+    int mask_batch = 1, mask_heads = 1;
+    float max_bias = 0.f;
 };
 
 // Returns false if (dk, dv) has no compiled instance.

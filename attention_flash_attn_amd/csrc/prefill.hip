@@ -31,6 +31,10 @@
 //    lets the O rescale be skipped for the whole wave on most tiles.
 //  * Row sums add the bf16-rounded probabilities two at a time (v_dot2), so O
 //    is an exact convex combination of V rows up to fp32 accumulation.
+//  * Additive mask (optional, IEEE fp16 [MB, MH, Sq, stride], head h of batch b
+//    reading mask[b % MB][h % MH] as in the page's kernel), times the head's
+//    ALiBi slope, is added after the softcap; each lane reads its query row's
+//    entries for a tile with 8-byte buffer loads one tile ahead.
 //  * Causal: tiles past the workgroup's last visible key are never loaded, a
 //    wave skips tiles wholly above its diagonal, and only tiles crossing the
 //    diagonal or the end of the keys evaluate the mask. Workgroups are
@@ -55,7 +59,18 @@ struct PrefillParams {
     float c_tanh;   // 2 * scale / softcap * log2 e  (softcap on: exponent of e^{2y})
     float c_cap;    // softcap * log2 e
     int xcd_remap;  // B * Hq is a multiple of 8
+    // additive mask (fp16 bits) and ALiBi
+    const uint16_t* __restrict__ mask;
+    long long mask_stride;  // elements between query rows
+    int mask_batch, mask_heads;
+    float max_bias;
+    int n_head_log2;
 };
+
+// 8-byte buffer load (4 fp16 mask entries); offsets past the resource read 0.
+extern "C" __device__ u32x2 llvm_amdgcn_raw_buffer_load_v2i32(i32x4 rsrc, int voffset, int soffset,
+                                                              int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
@@ -75,9 +90,10 @@ constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 #define ATTN_D256_CFG 32, 8, 2
 #endif
 
-template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool OF32>
+template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool ADDM, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillParams p) {
+    constexpr bool LOG2 = SOFTCAP || ADDM;  // scores converted to log2 units before the max
     constexpr int NT = NW * 64;
     constexpr int BM = NW * 32;             // query rows per workgroup
     constexpr int DVP = DV < 32 ? 32 : DV;  // V rows padded to a whole 32-row block of O^T
@@ -199,6 +215,39 @@ void prefill_kernel(PrefillParams p) {
     float m_run = -INFINITY;  // reference max of this lane's query (log2 units), same in both halves
     float l_run = 0.f;        // this lane's share of the running sum (its half of each key block)
     const int lim = CAUSAL ? min(p.Sk - 1, qi + shift) : p.Sk - 1;  // last visible key of this row
+
+    // additive mask: this lane's query row of slab mask[b % MB][h % MH]; rows past Sq read row Sq-1
+    i32x4 mrsrc = {0, 0, 0, 0};
+    uint32_t mrow_off = 0;
+    float ms2 = 0.f;  // slope * log2 e
+    // entries of tile t+1 load during tile t (MPF), except at head dims whose registers are full,
+    // where tile t's entries load right after its barrier (ahead of the next tile's copies)
+    constexpr bool MPF = ADDM && (DK < 192 || OCC == 1);
+    u32x2 mcur[KB][4], mnext[KB][4];
+    if constexpr (ADDM) {
+        const size_t slab = (size_t)p.Sq * (size_t)p.mask_stride;
+        const uint16_t* mb = p.mask + ((size_t)(b % p.mask_batch) * p.mask_heads + (h % p.mask_heads)) * slab;
+        mrsrc = make_buffer(mb, (uint32_t)(slab * 2));
+        mrow_off = (uint32_t)((size_t)min(qi, p.Sq - 1) * (size_t)p.mask_stride * 2);
+        // ALiBi slope: m0^(h+1) below n_head_log2, else m1^(2(h - n_head_log2) + 1), with
+        // m0 = 2^(-max_bias / n_head_log2) and m1 = 2^(-max_bias / (2 n_head_log2)); 1 when max_bias = 0
+        const float e = h < p.n_head_log2 ? -(float)(h + 1) * p.max_bias / (float)p.n_head_log2
+                                          : -(float)(2 * (h - p.n_head_log2) + 1) * p.max_bias /
+                                                (2.f * (float)p.n_head_log2);
+        ms2 = exp2_fast(e) * kLog2e;
+    }
+    auto mload = [&](int t, u32x2 (&m)[KB][4]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int key = t * BN + kb * 32 + g4 * 8 + half * 4;
+                m[kb][g4] = llvm_amdgcn_raw_buffer_load_v2i32(mrsrc, (int)(mrow_off + (uint32_t)key * 2u), 0, 0);
+            }
+    };
+    if constexpr (MPF) {
+        if (ntiles > 0) mload(0, mcur);
+    }
     // per-lane LDS byte offsets: K row col (both key blocks), 16-byte half `half`;
     // V^T rows half*4 + (lane&15)/4 of a 4-row transposing block, column
     // ((lane>>4)&1)*16 + (lane&3)*4 of a 32-column block
@@ -239,6 +288,22 @@ void prefill_kernel(PrefillParams p) {
                 }
             }
         }
+        if constexpr (ADDM) {
+            // log2-unit score plus slope * mask entry (fp16 -inf stays -inf)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f16x4 mv = __builtin_bit_cast(f16x4, mcur[kb][g4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = g4 * 4 + e;
+                        const float base = SOFTCAP ? sacc[kb][i] : sacc[kb][i] * p.c_score;
+                        sacc[kb][i] = __builtin_fmaf((float)mv[e], ms2, base);
+                    }
+                }
+            }
+        }
         if constexpr (MASK) {  // diagonal and last tiles only
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -256,8 +321,8 @@ void prefill_kernel(PrefillParams p) {
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
         }
         mx = halfwave_max(mx);
-        const float cs = SOFTCAP ? 1.f : p.c_score;
-        const float m_tile = SOFTCAP ? mx : mx * cs;
+        const float cs = LOG2 ? 1.f : p.c_score;
+        const float m_tile = LOG2 ? mx : mx * cs;
         // lazy reference update: only when the tile max exceeds the reference by > 2^tau
         const bool upd = m_tile > m_run + kTau;
         if (__builtin_amdgcn_ballot_w64(upd)) {
@@ -313,16 +378,29 @@ void prefill_kernel(PrefillParams p) {
     if (CAUSAL) t_full = min(t_full, max(0, (qt * BM + shift + 1) / BN));
     t_full = min(t_full, ntiles);
     auto step = [&](int t) {
-        wait_vmem();       // this wave's loads of tile t have landed in LDS
+        wait_vmem();       // this wave's loads of tile t (and its mask entries) have landed
         __syncthreads();   // ... and every other wave's; stage (t+1)&1 is free again
-        if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+        if constexpr (ADDM && !MPF) mload(t, mcur);
+        if (t + 1 < ntiles) {
+            issue(t + 1, (t + 1) & 1);
+            if constexpr (MPF) mload(t + 1, mnext);
+        }
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto next_mask = [&]() {
+        if constexpr (MPF) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) mcur[kb][g4] = mnext[kb][g4];
+        }
     };
 #pragma clang loop unroll(disable)
     for (int t = 0; t < t_full; ++t) {
         step(t);
         const char* kt = smem + (t & 1) * STAGE;
         tile(kt, kt + K_BYTES, t * BN, std::false_type{});
+        next_mask();
     }
 #pragma clang loop unroll(disable)
     for (int t = t_full; t < ntiles; ++t) {
@@ -330,6 +408,7 @@ void prefill_kernel(PrefillParams p) {
         const char* kt = smem + (t & 1) * STAGE;
         const bool skip = CAUSAL && (t * BN > q0 + 31 + shift);  // wave-uniform
         if (!skip) tile(kt, kt + K_BYTES, t * BN, std::true_type{});
+        next_mask();
     }
 
     // epilogue: sinks, normalisation, store
@@ -365,26 +444,35 @@ void prefill_kernel(PrefillParams p) {
     }
 }
 
-template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP>
+template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool ADDM>
 hipError_t launch_variant(PrefillParams p, bool of32, hipStream_t stream) {
     constexpr int BM = NW * 32;
     p.nqt = (p.Sq + BM - 1) / BM;
     const dim3 grid((unsigned)(p.nqt * p.Hq * p.B)), block(NW * 64);
     if (of32)
-        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, ADDM, true>), grid, block, 0, stream,
+                           p);
     else
-        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, ADDM, false>), grid, block, 0, stream,
+                           p);
     return hipGetLastError();
 }
 
-template <int DK, int DV, int BN, int NW, int OCC>
-hipError_t launch_inst(const PrefillParams& p, bool causal, bool softcap, bool of32, hipStream_t stream) {
+template <int DK, int DV, int BN, int NW, int OCC, bool ADDM>
+hipError_t launch_flags(const PrefillParams& p, bool causal, bool softcap, bool of32, hipStream_t stream) {
     if (causal) {
-        return softcap ? launch_variant<DK, DV, BN, NW, OCC, true, true>(p, of32, stream)
-                       : launch_variant<DK, DV, BN, NW, OCC, true, false>(p, of32, stream);
+        return softcap ? launch_variant<DK, DV, BN, NW, OCC, true, true, ADDM>(p, of32, stream)
+                       : launch_variant<DK, DV, BN, NW, OCC, true, false, ADDM>(p, of32, stream);
     }
-    return softcap ? launch_variant<DK, DV, BN, NW, OCC, false, true>(p, of32, stream)
-                   : launch_variant<DK, DV, BN, NW, OCC, false, false>(p, of32, stream);
+    return softcap ? launch_variant<DK, DV, BN, NW, OCC, false, true, ADDM>(p, of32, stream)
+                   : launch_variant<DK, DV, BN, NW, OCC, false, false, ADDM>(p, of32, stream);
+}
+
+// (BN, NW, OCC) without a mask; (BNM, NWM, OCCM) with one
+template <int DK, int DV, int BN, int NW, int OCC, int BNM = BN, int NWM = NW, int OCCM = OCC>
+hipError_t launch_inst(const PrefillParams& p, bool causal, bool softcap, bool of32, hipStream_t stream) {
+    if (p.mask != nullptr) return launch_flags<DK, DV, BNM, NWM, OCCM, true>(p, causal, softcap, of32, stream);
+    return launch_flags<DK, DV, BN, NW, OCC, false>(p, causal, softcap, of32, stream);
 }
 
 }  // namespace
@@ -419,6 +507,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     p.c_tanh = softcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
     p.c_cap = a.softcap * kLog2e;
     p.xcd_remap = ((a.B * a.Hq) % 8) == 0;
+    p.mask = (const uint16_t*)a.mask;
+    p.mask_stride = a.mask_stride;
+    p.mask_batch = a.mask_batch;
+    p.mask_heads = a.mask_heads;
+    p.max_bias = a.max_bias;
+    int nl2 = 1;
+    while (nl2 * 2 <= a.Hq) nl2 *= 2;
+    p.n_head_log2 = nl2;
     const bool of32 = a.o_f32 != 0, causal = a.causal != 0;
     switch (a.dk * 1000 + a.dv) {
         case 16016: return launch_inst<16, 16, 64, 4, 2>(p, causal, softcap, of32, stream);
@@ -427,7 +523,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         case 96096: return launch_inst<96, 96, 64, 4, 2>(p, causal, softcap, of32, stream);
         case 128128: return launch_inst<128, 128, ATTN_D128_CFG>(p, causal, softcap, of32, stream);
         case 192192: return launch_inst<192, 192, 32, 4, 2>(p, causal, softcap, of32, stream);
-        case 256256: return launch_inst<256, 256, ATTN_D256_CFG>(p, causal, softcap, of32, stream);
+        case 256256: return launch_inst<256, 256, ATTN_D256_CFG, 32, 4, 1>(p, causal, softcap, of32, stream);
         case 192128: return launch_inst<192, 128, 32, 4, 2>(p, causal, softcap, of32, stream);
         default: return hipErrorInvalidValue;
     }

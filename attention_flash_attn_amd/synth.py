@@ -91,6 +91,30 @@ def prefill_case(seed, B, Sq, Sk, Hq, Hkv, dk, dv, std=1.0, sinks=False):
     return {"q": q, "k": k, "v": v, "sinks": s}
 
 
+def mask_case(seed, MB, MH, Sq, Sk, width=None, kind="random", p_neg_inf=0.1, std=2.0):
+    """Additive fp16 masks [MB, MH, Sq, width] (width >= Sk, default Sk rounded up to a
+    multiple of 4; columns >= Sk hold 0).
+
+    kind "random": N(0, std^2) entries, a fraction p_neg_inf of them -inf.
+    kind "distance": the position-distance mask used with ALiBi slopes, with query
+    i at position Sk - Sq + i: entry -(pos_i - j) for keys j <= pos_i, -inf after
+    (causal structure carried by the mask itself).
+    """
+    width = (Sk + 3) // 4 * 4 if width is None else width
+    m = np.zeros((MB, MH, Sq, width), dtype=np.float32)
+    if kind == "random":
+        rng = np.random.Generator(np.random.PCG64([seed, 7]))
+        m[..., :Sk] = rng.standard_normal((MB, MH, Sq, Sk), dtype=np.float32) * std
+        m[..., :Sk][rng.random((MB, MH, Sq, Sk)) < p_neg_inf] = -np.inf
+    elif kind == "distance":
+        pos = np.arange(Sq)[:, None] + (Sk - Sq)
+        j = np.arange(Sk)[None, :]
+        m[..., :Sk] = np.where(j <= pos, -(pos - j).astype(np.float32), -np.inf)
+    else:
+        raise ValueError(kind)
+    return m.astype(np.float16)
+
+
 def paged_case(seed, B, Hq, Hkv, dk, dv, len_lo, len_hi, block_size=64, max_blocks=None,
                Sq=1, std=1.0, sinks=False, lens=None):
     """Paged-cache decode inputs.

@@ -5,6 +5,7 @@
  *
  *     x_j  = scale * <q_i, k_j>                  raw dot product, scaled afterwards
  *     x_j  = softcap * tanh(x_j / softcap)       only when softcap != 0
+ *     x_j += slope_h * mask[i, j]                only with an additive mask (attn_prefill_fwd_masked)
  *     keys excluded by the mask are dropped
  *     o_i  = sum_j e^{x_j} v_j / (sum_j e^{x_j} + e^{sink_h})     (sink term only with sinks)
  *
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum attn_status {
     ATTN_OK = 0,
@@ -93,6 +94,32 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v,
                              int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv,
                              float scale, int causal, float softcap, const float* sinks,
                              void* stream);
+
+/*
+ * Prefill with an additive mask and optional ALiBi slopes (the mask and
+ * max_bias arguments of the fa.metal tensor kernel on the "ggml-metal: FA
+ * tensor path" page: the mask entry, times the head's slope, is added to the
+ * score after the softcap). Arguments as attn_prefill_fwd, plus:
+ *   mask  IEEE fp16 [mask_batch, mask_heads, Sq, mask_row_stride], contiguous,
+ *         16-byte aligned; entry [b % mask_batch, h % mask_heads, i, j] is added
+ *         for query i, key j of batch b and query head h (columns j >= Sk are
+ *         ignored). -inf drops the key. NULL = no mask (then this call is
+ *         attn_prefill_fwd; max_bias has nothing to scale).
+ *   mask_batch, mask_heads >= 1 (1 = shared by all batch entries / heads).
+ *   mask_row_stride >= Sk, a multiple of 4 (elements between query rows);
+ *         one [Sq, mask_row_stride] slab must be under 4 GiB.
+ *   max_bias >= 0: ALiBi. Head h's slope is m0^(h+1) for h < n, else
+ *         m1^(2(h - n) + 1), with n the largest power of two <= Hq,
+ *         m0 = 2^(-max_bias / n), m1 = 2^(-max_bias / (2n)); 0 gives slope 1.
+ * causal may be combined with the mask (both apply).
+ */
+attn_status attn_prefill_fwd_masked(const void* q, const void* k, const void* v,
+                                    void* o, int o_dtype, float* lse,
+                                    int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv,
+                                    float scale, int causal, float softcap, const float* sinks,
+                                    const void* mask, int mask_batch, int mask_heads,
+                                    int64_t mask_row_stride, float max_bias,
+                                    void* stream);
 
 /*
  * Workspace (bytes) that attn_decode_fwd needs for these sizes: the split-KV

@@ -30,7 +30,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = binding.load_library()
     names = declared_functions()
-    assert {"attn_prefill_fwd", "attn_decode_fwd", "attn_decode_workspace_bytes"} <= set(names)
+    assert {"attn_prefill_fwd", "attn_prefill_fwd_masked", "attn_decode_fwd",
+            "attn_decode_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "symbol %s missing from libattn.so" % n
 
@@ -70,6 +71,35 @@ def prefill(lib, **kw):
 def test_prefill_rejects(kw, status):
     lib = binding.load_library()
     assert prefill(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def prefill_masked(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, od=0, lse=None, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, dk=64, dv=64,
+             scale=0.125, causal=0, softcap=0.0, sinks=None, mask=FAKE, mb=1, mh=1, ms=8, max_bias=0.0,
+             stream=None)
+    a.update(kw)
+    return lib.attn_prefill_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["od"], a["lse"], a["B"], a["Hq"],
+                                       a["Hkv"], a["Sq"], a["Sk"], a["dk"], a["dv"], a["scale"], a["causal"],
+                                       a["softcap"], a["sinks"], a["mask"], a["mb"], a["mh"], a["ms"],
+                                       a["max_bias"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),
+    (dict(mb=0), 1),
+    (dict(mh=0), 1),
+    (dict(ms=6), 1),                                   # row stride below Sk
+    (dict(ms=10), 1),                                  # not a multiple of 4
+    (dict(mask=ctypes.c_void_p(0x10008)), 1),          # not 16-byte aligned
+    (dict(max_bias=-1.0), 1),
+    (dict(max_bias=float("inf")), 1),
+    (dict(Sq=1 << 20, Sk=1 << 20, ms=1 << 20), 2),     # one mask slab of 2 TiB
+    (dict(dk=48, dv=48), 2),
+])
+def test_prefill_masked_rejects(kw, status):
+    lib = binding.load_library()
+    assert prefill_masked(lib, **kw) == status
     assert lib.attn_last_error().decode() != ""
 
 

@@ -13,7 +13,7 @@ from gpu_util import check_close, dev, dev_bf16, host
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL = -math.log(1 - 2.0 ** -9) + 1e-5
+LSE_TOL = -math.log(1 - 2.0 ** -8) + 1e-5
 
 
 def run_prefill(case, scale, causal, softcap, o_dtype, with_lse=True):
@@ -42,9 +42,11 @@ def check_case(B, Sq, Sk, Hq, Hkv, dk, dv, causal=False, softcap=0.0, sinks=Fals
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(got_l), fin)
     if fin.any():
-        # The kernel sums the bf16-rounded probabilities (relative error <= 2^-9 each), so
-        # its normaliser Z' = Z (1 + d) with |d| <= 2^-9 and |ln Z' - ln Z| <= -ln(1 - 2^-9)
-        # = 1.955e-3; fp32 score and exp2/log2 errors add well under 1e-5.
+        # The kernel sums the bf16-rounded probabilities. bf16 keeps 8 significand bits, so
+        # round-to-nearest has relative error <= 2^-8 per probability, the normaliser is
+        # Z' = Z (1 + d) with |d| <= 2^-8 (reached when one probability dominates) and
+        # |ln Z' - ln Z| <= -ln(1 - 2^-8) = 3.914e-3; fp32 score and exp2/log2 errors add
+        # well under 1e-5.
         assert np.abs(got_l[fin] - rl[fin]).max() < LSE_TOL
 
 
