@@ -230,14 +230,18 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale, causal=False
 
 
 def decode_gathered(q, k_rows, v_rows, row_index, key_pos, q_pos, scale,
-                    causal=True, softcap=0.0, sinks=None, tokens=None):
+                    causal=True, softcap=0.0, sinks=None, tokens=None, k_cur=None, v_cur=None):
     """Decode over rows gathered from a row cache (one shared KV head).
 
     q [T, Hq, dk]; k_rows [R, dk] and v_rows [R, dv] are the key and value
     fields of the cache rows; row_index [T, n_sel] selects the rows each token
     attends to; key_pos [T, n_sel] (float) is each selected key's absolute
     position and q_pos [T] the token's own. When causal, a key is live iff
-    key_pos <= q_pos. Returns (o [nt, Hq, dv], lse [nt, Hq]) in float64.
+    key_pos <= q_pos. k_cur [T, dk] / v_cur [T, dv] (both or neither) append the
+    token's own row as one more key at position q_pos, always live: the
+    "MLA Decode Attention Kernel API Reference" page, Dimensions (n_keys =
+    n_prior + 1, the selected prior plus the current token) and kv_row_cur.
+    Returns (o [nt, Hq, dv], lse [nt, Hq]) in float64.
     """
     q = _as_f64(q)
     k_rows = np.asarray(k_rows)
@@ -255,6 +259,10 @@ def decode_gathered(q, k_rows, v_rows, row_index, key_pos, q_pos, scale,
         K = _as_f64(k_rows[r])
         V = _as_f64(v_rows[r])
         live_row = (key_pos[t] <= float(q_pos[t])) if causal else np.ones(len(r), dtype=bool)
+        if k_cur is not None:
+            K = np.concatenate([K, _as_f64(np.asarray(k_cur)[t])[None, :]])
+            V = np.concatenate([V, _as_f64(np.asarray(v_cur)[t])[None, :]])
+            live_row = np.concatenate([live_row, [True]])
         for h in range(Hq):
             sink = None if sinks is None else float(np.asarray(sinks, dtype=np.float64)[h])
             ob, lb = attend_rows(q[t, h][None, :], K, V, scale, softcap, sink, live_row[None, :])

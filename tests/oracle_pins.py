@@ -332,6 +332,30 @@ def pin_gathered(orc):
     _close(o, o2, 1e-13, "selection order")
 
 
+def pin_gathered_current_row(orc):
+    """The current token's row appended as key n_prior (always live) equals the same row
+    stored in the cache and selected with position q_pos; and when every prior key lies
+    after the token, the current row is the only live key, so o is its value exactly."""
+    rng = _rng(71)
+    T, Hq, d, R, n_sel = 3, 4, 8, 40, 6
+    rows = _rand(rng, R, d)
+    q = _rand(rng, T, Hq, d)
+    cur = _rand(rng, T, d)
+    q_pos = np.array([20, 33, 9])
+    sel = np.stack([rng.choice(R, n_sel, replace=False) for _ in range(T)])
+    kpos = np.stack([rng.choice(int(q_pos[t]), n_sel, replace=False) for t in range(T)]).astype(np.float64)
+    o1, l1 = orc.decode_gathered(q, rows, rows[:, :5], sel, kpos, q_pos, 0.3, k_cur=cur, v_cur=cur[:, :5])
+    rows2 = np.concatenate([rows, cur])                       # the current rows stored at R .. R+T-1
+    sel2 = np.concatenate([sel, (R + np.arange(T))[:, None]], axis=1)
+    kpos2 = np.concatenate([kpos, q_pos[:, None].astype(np.float64)], axis=1)
+    o2, l2 = orc.decode_gathered(q, rows2, rows2[:, :5], sel2, kpos2, q_pos, 0.3)
+    _close(o1, o2, 1e-13, "appended current row vs stored and selected")
+    _close(l1, l2, 1e-13, "lse with the current row")
+    future = q_pos[:, None] + 1.0 + np.arange(n_sel)[None, :]
+    o3, _ = orc.decode_gathered(q, rows, rows[:, :5], sel, future, q_pos, 0.3, k_cur=cur, v_cur=cur[:, :5])
+    _close(o3, np.broadcast_to(cur[:, None, :5], o3.shape), 1e-15, "only the current row is live")
+
+
 # ---------------------------------------------------------------- additive mask, ALiBi
 def pin_alibi_slopes_published(orc):
     """The ALiBi slope schedule (Press, Smith and Lewis, "Train Short, Test Long"):

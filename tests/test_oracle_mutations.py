@@ -39,6 +39,9 @@ MUTATIONS = {
     "alibi_exponent_off_by_one": ("m0 ** (h + 1)", "m0 ** h"),
     "alibi_m1_base": ("m1 = 2.0 ** (-max_bias / 2.0 / n_log2)", "m1 = 2.0 ** (-max_bias / n_log2)"),
     "alibi_slope_ignored": ("bias = slopes[h] * mrows", "bias = mrows"),
+    "current_row_masked": ("live_row = np.concatenate([live_row, [True]])",
+                           "live_row = np.concatenate([live_row, [False]])"),
+    "current_row_wrong_token": ("_as_f64(np.asarray(k_cur)[t])[None, :]", "_as_f64(np.asarray(k_cur)[0])[None, :]"),
 }
 
 
