@@ -69,7 +69,7 @@ def load_library():
                                         c_float, c_int, c_float, c_void_p,
                                         c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_int, ctypes.c_int64,
-                                        c_void_p, c_size_t, c_void_p]
+                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         _LIB = lib
         return lib
 
@@ -178,12 +178,14 @@ def attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk_max, dk, dv):
 
 def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=False, softcap=0.0,
                     sinks=None, block_table=None, seq_lens=None, row_index=None, key_pos=None,
-                    q_pos=None, kv_row_stride=0, Hkv=None, dk=None, dv=None, stream=None):
+                    q_pos=None, kv_row_stride=0, Hkv=None, dk=None, dv=None, k_cur=None, v_cur=None,
+                    stream=None):
     """Paged mode: k_cache [n_blocks,Hkv,bs,dk], v_cache [n_blocks,Hkv,bs,dv], block_table
     [B,max_blocks] int32, seq_lens [B] int32. Gathered mode: k_cache / v_cache are 2-D row
     views [rows, width] sharing one row stride (e.g. kv[:, :dk] and kv[:, 64:]), with
-    row_index [B,n_sel] int32, key_pos [B,n_sel] fp32, q_pos [B] int32; dk defaults to q's
-    width and dv to o's. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv]."""
+    row_index [B,n_sel] int32, key_pos [B,n_sel] fp32, q_pos [B] int32, and optionally the
+    tokens' own rows k_cur / v_cur as 2-D row views [B, width] with the same row stride;
+    dk defaults to q's width and dv to o's. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv]."""
     import torch
     lib = load_library()
     B, Sq, Hq, qdk = q.shape
@@ -209,6 +211,16 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
             kv_row_stride = k_cache.stride(0)
         if v_cache.stride(0) != kv_row_stride:
             raise AttnError(ATTN_ERR_INVALID_ARG, "k_cache and v_cache rows must share one stride")
+        if (k_cur is None) != (v_cur is None):
+            raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur and v_cur go together")
+        if k_cur is not None:
+            kcp, vcp = _row_ptr(k_cur, "k_cur"), _row_ptr(v_cur, "v_cur")
+            if k_cur.stride(0) != kv_row_stride or v_cur.stride(0) != kv_row_stride:
+                raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur / v_cur rows must have the cache's row stride")
+            if k_cur.shape[0] < B or v_cur.shape[0] < B:
+                raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur / v_cur need one row per token")
+    if paged or k_cur is None:
+        kcp, vcp = None, None
     st = lib.attn_decode_fwd(_ptr(q, "q", torch.bfloat16), kp, vp, _ptr(o, "o"), _odtype(o),
                              B, Hq, Hkv, Sq, int(Sk_max), dk, dv, float(scale), int(bool(causal)),
                              float(softcap), _ptr(sinks, "sinks", torch.float32, True),
@@ -217,5 +229,5 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
                              _ptr(row_index, "row_index", torch.int32, True),
                              _ptr(key_pos, "key_pos", torch.float32, True),
                              _ptr(q_pos, "q_pos", torch.int32, True), n_sel, int(kv_row_stride),
-                             _ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+                             kcp, vcp, _ptr(workspace, "workspace"), ws_bytes, _stream(stream))
     _check(st)

@@ -146,7 +146,8 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
                             float softcap, const float* sinks, const int32_t* block_table, int block_size,
                             int max_blocks_per_seq, const int32_t* seq_lens, const int32_t* row_index,
                             const float* key_pos, const int32_t* q_pos, int n_sel, int64_t kv_row_stride,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            const void* k_cur, const void* v_cur, void* workspace, size_t workspace_bytes,
+                            void* stream) {
     if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o are required");
     attn_status st = check_common(B, Hq, Hkv, Sq, dk, dv, scale, softcap, o_dtype);
     if (st != ATTN_OK) return st;
@@ -163,14 +164,21 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
             return fail(ATTN_ERR_INVALID_ARG, "block_size must be 16, 32, 64 or 128 (got %d)", block_size);
         if (max_blocks_per_seq <= 0 || (int64_t)max_blocks_per_seq * block_size < Sk_max)
             return fail(ATTN_ERR_INVALID_ARG, "max_blocks_per_seq * block_size must cover Sk_max");
-        if (Sq * (Hq / Hkv) > 32)
-            return fail(ATTN_ERR_UNSUPPORTED, "paged decode needs Sq * (Hq / Hkv) <= 32 (got %d)", Sq * (Hq / Hkv));
+        if ((int64_t)Sq * (Hq / Hkv) > (1 << 20))
+            return fail(ATTN_ERR_UNSUPPORTED, "paged decode needs Sq * (Hq / Hkv) <= 2^20");
+        if (k_cur || v_cur) return fail(ATTN_ERR_INVALID_ARG, "k_cur / v_cur apply to gathered mode only");
     } else {
         if (!key_pos || !q_pos) return fail(ATTN_ERR_INVALID_ARG, "gathered mode needs key_pos and q_pos");
         if (Hkv != 1 || Sq != 1) return fail(ATTN_ERR_INVALID_ARG, "gathered mode needs Hkv == 1 and Sq == 1");
         if (n_sel <= 0 || n_sel != Sk_max) return fail(ATTN_ERR_INVALID_ARG, "gathered mode needs n_sel == Sk_max > 0");
         if (kv_row_stride < dk || kv_row_stride < dv || kv_row_stride % 8 != 0)
             return fail(ATTN_ERR_INVALID_ARG, "kv_row_stride must be a multiple of 8 and >= dk, dv");
+        if ((k_cur == nullptr) != (v_cur == nullptr))
+            return fail(ATTN_ERR_INVALID_ARG, "k_cur and v_cur go together");
+        if (k_cur && (!aligned16(k_cur) || !aligned16(v_cur)))
+            return fail(ATTN_ERR_INVALID_ARG, "k_cur and v_cur must be 16-byte aligned");
+        if (k_cur && v_cache == k_cache && v_cur != k_cur)
+            return fail(ATTN_ERR_INVALID_ARG, "v_cache == k_cache needs v_cur == k_cur (value = key-row prefix)");
     }
     if (!attn::decode_supported(dk, dv, gathered))
         return fail(ATTN_ERR_UNSUPPORTED, "%s decode (dk, dv) = (%d, %d) is not built", gathered ? "gathered" : "paged",
@@ -209,6 +217,8 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
     a.q_pos = q_pos;
     a.n_sel = n_sel;
     a.row_stride = kv_row_stride;
+    a.k_cur = k_cur;
+    a.v_cur = v_cur;
     a.workspace = workspace;
     hipError_t e = attn::launch_decode(a, pl, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));

@@ -50,6 +50,8 @@ struct DecodeArgs {
     const int32_t* row_index;
     const float* key_pos;
     const int32_t* q_pos;
+    const void* k_cur = nullptr;  // gathered mode: token t's own key / value row (NULL: none)
+    const void* v_cur = nullptr;
     int n_sel;
     int64_t row_stride;
     // split-KV scratch

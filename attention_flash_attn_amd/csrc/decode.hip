@@ -32,6 +32,7 @@ struct SplitParams {
     const int32_t* __restrict__ block_table;
     const int32_t* __restrict__ seq_lens;
     int B, Hq, Hkv, Sq, group, nq, bs_log2, max_blocks;
+    int ncg;  // groups of 32 query columns per KV head (one workgroup each)
     int n_split, split_len;
     float c_score, c_tanh, c_cap;
     int causal, softcap_on;
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
     const int lane = threadIdx.x, grp = lane >> 4, c16 = lane & 15;
     // split-major grid: every (KV head, sequence) pair of split 0 first, then split 1, ...,
     // so the last work dispatched belongs to the longest sequences' final (often partial) splits
-    const int split = blockIdx.z, g = blockIdx.x, b = blockIdx.y;
+    const int split = blockIdx.z, g = blockIdx.x / p.ncg, cg0 = (blockIdx.x % p.ncg) * 32, b = blockIdx.y;
     const int L = p.seq_lens[b];
     const int start = split * p.split_len;
     if (start >= L) return;  // the combine pass only reads splits that start below L
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
     int lim[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        const int colq = cb * 16 + c16;
+        const int colq = cg0 + cb * 16 + c16;
         const bool ok = colq < p.nq;
         const int si = ok ? colq / p.group : 0;
         const int h = g * p.group + (ok ? colq % p.group : 0);
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const float l_tot = quarterwave_sum(l_run[cb]);
-        const int colq = cb * 16 + c16;
+        const int colq = cg0 + cb * 16 + c16;
         if (colq < p.nq) {
             const int si = colq / p.group;
             const int h = g * p.group + colq % p.group;
@@ -293,13 +294,19 @@ struct GatherParams {
     const int32_t* __restrict__ row_index;
     const float* __restrict__ key_pos;
     const int32_t* __restrict__ q_pos;
+    // token t's own key row at kc + kcur_off + t * row_stride, value row at vc + vcur_off + ...
+    // (element offsets from the cache bases, so every gather address derives from one base pointer)
+    long long kcur_off, vcur_off;
+    int has_cur;
     int T, Hq, n_sel, n_split, split_len;
     long long row_stride;  // elements
     float c_score, c_tanh, c_cap;
     int causal, softcap_on;
 };
 
-constexpr int kGatherMaxSplit = 1024;  // keys per split the LDS index table holds
+// keys per split the LDS index table holds: a split of up to 1024 selected keys, plus the
+// token's own row in the last split, rounded up to whole 32-key steps
+constexpr int kGatherMaxSplit = 1024 + 32;
 
 #ifndef ATTN_GPF_K
 #define ATTN_GPF_K 4  // K fragments read ahead of their MFMA
@@ -343,12 +350,19 @@ void decode_gathered_split_kernel(GatherParams p) {
     const int split = blockIdx.x, hgrp = blockIdx.y, t = blockIdx.z;
     const int start = split * p.split_len;
     const int end = min(p.n_sel, start + p.split_len);
-    const int nk = end - start;
+    const int nsel = end - start;
+    // the last split also takes the token's own row (n_keys = n_prior + 1), always live
+    const int has_cur = (p.has_cur && split == p.n_split - 1) ? 1 : 0;
+    const int nk = nsel + has_cur;
     const float qpos = (float)p.q_pos[t];
 
-    for (int i = tid; i < nk; i += NT) {
+    for (int i = tid; i < nsel; i += NT) {
         srow[i] = p.row_index[(size_t)t * p.n_sel + start + i];
         spos[i] = p.key_pos[(size_t)t * p.n_sel + start + i];
+    }
+    if (has_cur && tid == 0) {
+        srow[nsel] = -1;  // rows come from kcur / vcur
+        spos[nsel] = qpos;
     }
     __syncthreads();
 
@@ -377,11 +391,12 @@ void decode_gathered_split_kernel(GatherParams p) {
             const int r = off / PITCH;
             const int c = ((off - r * PITCH) >> 4) ^ sw(r);
             const int kr = min(i * 32 + r, nk - 1);
-            const size_t rb = (size_t)srow[kr] * (size_t)p.row_stride;
-            load_lds16(p.kc + rb + c * 8, sb + sg * 1024);
+            const int row = srow[kr];
+            const long long rb = (long long)(row >= 0 ? row : t) * p.row_stride;
+            load_lds16(p.kc + (row >= 0 ? rb : p.kcur_off + rb) + c * 8, sb + sg * 1024);
             if constexpr (!VK) {
                 // value rows use the same layout; chunks past the value width repeat earlier ones
-                load_lds16(p.vc + rb + (c % (DV / 8)) * 8, sb + SSTAGE + sg * 1024);
+                load_lds16(p.vc + (row >= 0 ? rb : p.vcur_off + rb) + (c % (DV / 8)) * 8, sb + SSTAGE + sg * 1024);
             }
         }
     };
@@ -604,7 +619,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
 
 template <int DK, int DV>
 hipError_t launch_paged(const SplitParams& sp, dim3 grid, hipStream_t stream) {
-    if (sp.nq <= 16)
+    if (sp.nq <= 16)  // one group of up to 16 columns; otherwise groups of 32
         hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 1>), grid, dim3(64), 0, stream, sp);
     else
         hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 2>), grid, dim3(64), 0, stream, sp);
@@ -687,6 +702,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     sp.Sq = a.Sq;
     sp.group = a.Hq / a.Hkv;
     sp.nq = a.Sq * sp.group;
+    sp.ncg = (sp.nq + 31) / 32;
     int lg = 0;
     while ((1 << lg) < a.block_size) ++lg;
     sp.bs_log2 = lg;
@@ -710,6 +726,9 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         gp.row_index = a.row_index;
         gp.key_pos = a.key_pos;
         gp.q_pos = a.q_pos;
+        gp.has_cur = a.k_cur != nullptr;
+        gp.kcur_off = gp.has_cur ? (long long)((const uint16_t*)a.k_cur - (const uint16_t*)a.k_cache) : 0;
+        gp.vcur_off = gp.has_cur ? (long long)((const uint16_t*)a.v_cur - (const uint16_t*)a.v_cache) : 0;
         gp.T = a.B;
         gp.Hq = a.Hq;
         gp.n_sel = a.n_sel;
@@ -731,7 +750,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         if (e != hipSuccess) return e;
         return launch_combine(a, pl, ws_o, ws_ml, nullptr, stream);
     }
-    const dim3 grid((unsigned)a.Hkv, (unsigned)a.B, (unsigned)pl.n_split);
+    const dim3 grid((unsigned)(a.Hkv * sp.ncg), (unsigned)a.B, (unsigned)pl.n_split);
     switch (a.dk * 1000 + a.dv) {
         case 16016: e = launch_paged<16, 16>(sp, grid, stream); break;
         case 32032: e = launch_paged<32, 32>(sp, grid, stream); break;

@@ -145,6 +145,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  *     slot j % block_size of physical block block_table[b, j / block_size];
  *   seq_lens int32 [B] on the device, each in [0, Sk_max]; sequence b has keys
  *     [0, seq_lens[b]). block_size must be 16, 32, 64 or 128 (multiple of 16).
+ *   Any Sq: query columns (Sq * Hq / Hkv per KV head, e.g. several tokens of a
+ *     speculative draft) are processed in groups of 32.
  *   The caller guarantees table entries for j < seq_lens[b] are valid blocks.
  *
  * Gathered mode (row_index != NULL, block_table == NULL): Hkv must be 1 and Sq 1.
@@ -157,6 +159,12 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  *   q_pos    int32 [B]: position of token b. With causal, key j is live iff
  *     key_pos[b, j] <= q_pos[b]; without causal every selected key is live.
  *   Sk_max must equal n_sel.
+ *   k_cur, v_cur (optional, both or neither): bf16 rows [B, kv_row_stride]
+ *     holding token b's own key (first dk columns of k_cur row b) and value
+ *     (first dv of v_cur row b); they join the selected rows as one more key at
+ *     position q_pos[b], always live (the page's n_keys = n_prior + 1 with
+ *     kv_row_cur). With v_cache == k_cache, v_cur must equal k_cur. NULL in
+ *     paged mode.
  *
  *   workspace: device buffer of at least attn_decode_workspace_bytes(...) bytes,
  *     16-byte aligned, owned by the caller; contents on entry do not matter.
@@ -170,6 +178,7 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
                             const int32_t* seq_lens,
                             const int32_t* row_index, const float* key_pos, const int32_t* q_pos,
                             int n_sel, int64_t kv_row_stride,
+                            const void* k_cur, const void* v_cur,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 

@@ -106,12 +106,13 @@ def test_prefill_masked_rejects(kw, status):
 def decode(lib, **kw):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, od=0, B=2, Hq=8, Hkv=1, Sq=1, Sk_max=100, dk=128, dv=128,
              scale=0.1, causal=0, softcap=0.0, sinks=None, table=FAKE, bs=64, maxb=2, lens=FAKE,
-             rows=None, kpos=None, qpos=None, n_sel=0, stride=0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+             rows=None, kpos=None, qpos=None, n_sel=0, stride=0, kcur=None, vcur=None, ws=FAKE, ws_bytes=1 << 30,
+             stream=None)
     a.update(kw)
     return lib.attn_decode_fwd(a["q"], a["kc"], a["vc"], a["o"], a["od"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
                                a["Sk_max"], a["dk"], a["dv"], a["scale"], a["causal"], a["softcap"], a["sinks"],
                                a["table"], a["bs"], a["maxb"], a["lens"], a["rows"], a["kpos"], a["qpos"],
-                               a["n_sel"], a["stride"], a["ws"], a["ws_bytes"], a["stream"])
+                               a["n_sel"], a["stride"], a["kcur"], a["vcur"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -123,13 +124,18 @@ def decode(lib, **kw):
     (dict(maxb=1), 1),                                      # table too short for Sk_max
     (dict(ws_bytes=16), 1),
     (dict(ws=None), 1),
-    (dict(Hq=64, Hkv=1), 2),                                # group of 64 > 32 query columns
+    (dict(Sq=1 << 12, Hq=512, Hkv=1), 2),                   # 2^21 query columns per KV head
+    (dict(kcur=FAKE, vcur=FAKE), 1),                        # current rows in paged mode
     (dict(dk=100, dv=100), 2),
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, Hkv=2, Hq=8), 1),
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=128), 2),          # gathered (128,128)
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=576, dk=576, dv=512, Sq=2), 1),
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=99, stride=128), 1),
     (dict(table=None, rows=FAKE, kpos=None, qpos=FAKE, n_sel=100, stride=128), 1),
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=576, dk=576, dv=512, Hq=128,
+          kcur=FAKE), 1),                                   # k_cur without v_cur
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=576, dk=576, dv=512, Hq=128,
+          kcur=FAKE, vcur=ctypes.c_void_p(0x20000)), 1),    # v_cache == k_cache but v_cur != k_cur
 ])
 def test_decode_rejects(kw, status):
     lib = binding.load_library()

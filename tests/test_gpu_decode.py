@@ -96,7 +96,8 @@ def test_config4_full_size_sampled():
 
 
 # ---------------------------------------------------------------- gathered rows (MLA-style)
-def run_gathered(case, Hq, dk, dv, scale, causal=True, softcap=0.0, sinks=None, o_dtype="bf16", v_offset=0):
+def run_gathered(case, Hq, dk, dv, scale, causal=True, softcap=0.0, sinks=None, o_dtype="bf16", v_offset=0,
+                 cur=None):
     kv = dev_bf16(case["kv"])
     q = dev_bf16(case["q"]).view(case["q"].shape[0], 1, Hq, dk)
     T, n_sel = case["row_index"].shape
@@ -105,30 +106,38 @@ def run_gathered(case, Hq, dk, dv, scale, causal=True, softcap=0.0, sinks=None, 
     ws = torch.empty(nbytes, device="cuda", dtype=torch.uint8)
     k_rows = kv[:, :dk] if v_offset == 0 else kv[:, :dk]
     v_rows = kv[:, v_offset:v_offset + dv]
+    k_cur = v_cur = None
+    if cur is not None:
+        cd = dev_bf16(cur)
+        k_cur, v_cur = cd[:, :dk], cd[:, v_offset:v_offset + dv]
     binding.attn_decode_fwd(q, k_rows, v_rows, o, ws, scale=scale, Sk_max=n_sel, causal=causal, softcap=softcap,
                             sinks=None if sinks is None else dev(sinks), row_index=dev(case["row_index"]),
-                            key_pos=dev(case["key_pos"]), q_pos=dev(case["q_pos"]), dk=dk, dv=dv)
+                            key_pos=dev(case["key_pos"]), q_pos=dev(case["q_pos"]), dk=dk, dv=dv,
+                            k_cur=k_cur, v_cur=v_cur)
     torch.cuda.synchronize()
     return o[:, 0]
 
 
 def check_gathered(T, Hq, n_rows, n_sel, causal=True, softcap=0.0, sinks=False, o_dtype="f32", future=0,
-                   v_offset=0, seed=300, shuffle=False):
+                   v_offset=0, seed=300, shuffle=False, with_cur=False):
     dk, dv = 576, 512
-    print("gathered T=%d Hq=%d rows=%d n_sel=%d causal=%d softcap=%g sinks=%d %s future=%d v_offset=%d" %
-          (T, Hq, n_rows, n_sel, causal, softcap, sinks, o_dtype, future, v_offset), flush=True)
+    print("gathered T=%d Hq=%d rows=%d n_sel=%d causal=%d softcap=%g sinks=%d %s future=%d v_offset=%d cur=%d" %
+          (T, Hq, n_rows, n_sel, causal, softcap, sinks, o_dtype, future, v_offset, with_cur), flush=True)
     case = synth.gathered_case(seed, T, Hq, dk, dv, n_rows, n_sel, row_dim=576, sinks=sinks, future_keys=future)
     if shuffle:
         perm = np.random.default_rng(seed).permutation(n_sel)
         case["row_index"] = np.ascontiguousarray(case["row_index"][:, perm])
         case["key_pos"] = np.ascontiguousarray(case["key_pos"][:, perm])
     scale = 1.0 / math.sqrt(dk)
-    o = run_gathered(case, Hq, dk, dv, scale, causal, softcap, case["sinks"], o_dtype, v_offset)
+    cur = synth.normal_bf16(seed, 9, (T, 576)) if with_cur else None
+    o = run_gathered(case, Hq, dk, dv, scale, causal, softcap, case["sinks"], o_dtype, v_offset, cur)
     kv = case["kv"]
     ro, _ = oracle.decode_gathered(case["q"], kv[:, :dk], kv[:, v_offset:v_offset + dv], case["row_index"],
                                    case["key_pos"], case["q_pos"], scale, causal=causal, softcap=softcap,
-                                   sinks=case["sinks"])
-    return check_close(host(o), ro, o_dtype, "gathered decode")
+                                   sinks=case["sinks"], k_cur=None if cur is None else cur[:, :dk],
+                                   v_cur=None if cur is None else cur[:, v_offset:v_offset + dv])
+    check_close(host(o), ro, o_dtype, "gathered decode")
+    return host(o), ro
 
 
 def test_gathered_small_and_ragged():
@@ -153,5 +162,27 @@ def test_gathered_softcap_sinks_order_and_layout():
 def test_config5_full_size():
     c = synth.CONFIGS["c5_gathered_mla_decode"]
     print("full-size c5 gathered decode", flush=True)
-    err, cos = check_gathered(c["T"], c["Hq"], c["n_rows"], c["n_sel"], o_dtype="bf16", seed=c["seed"])
-    print("config 5: max err %.3g cos %.8f" % (err, cos))
+    o, ro = check_gathered(c["T"], c["Hq"], c["n_rows"], c["n_sel"], o_dtype="bf16", seed=c["seed"])
+    print("config 5: max err %.3g" % np.abs(o - ro).max())
+
+
+def test_gathered_current_row():
+    """The token's own row joins the selected rows as key n_prior (always live)."""
+    check_gathered(5, 128, 4096, 100, with_cur=True, seed=320)                    # one ragged split + 1
+    check_gathered(3, 64, 4096, 256, with_cur=True, seed=321)                     # 257 keys: one extra step
+    check_gathered(4, 128, 8192, 2048, with_cur=True, future=64, o_dtype="bf16", seed=322)
+    check_gathered(3, 128, 4096, 300, with_cur=True, v_offset=64, softcap=30.0, sinks=True, seed=323)
+
+
+def test_gathered_only_current_row_live():
+    """Every selected key lies after the token: the output is the current row's value."""
+    o, ro = check_gathered(3, 64, 2048, 96, with_cur=True, future=96, seed=324)
+    cur = synth.bf16_bits_to_f32(synth.normal_bf16(324, 9, (3, 576)))
+    np.testing.assert_allclose(ro, np.broadcast_to(cur[:, None, :512], ro.shape), rtol=0, atol=1e-12)
+
+
+def test_paged_many_query_columns():
+    """Sq * Hq / Hkv > 32 query columns per KV head (several draft tokens): column groups of 32."""
+    check_paged(3, 64, 8, 128, 128, 200, 700, Sq=8, causal=True, seed=330)         # 64 columns
+    check_paged(2, 32, 2, 64, 64, 100, 400, Sq=5, causal=True, o_dtype="bf16", seed=331)  # 80 columns
+    check_paged(2, 16, 1, 256, 256, 150, 300, Sq=3, causal=False, softcap=10.0, sinks=True, seed=332)
