@@ -9,7 +9,7 @@ missing.
 from .binding import (  # noqa: F401
     AttnError,
     attn_prefill_fwd,
-    attn_prefill_fwd_masked,
+    attn_prefill_fwd_ex,
     attn_decode_fwd,
     attn_decode_workspace_bytes,
     attn_status_string,

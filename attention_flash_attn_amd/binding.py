@@ -21,6 +21,7 @@ ATTN_ERR_UNSUPPORTED = 2
 ATTN_ERR_HIP = 3
 ATTN_BF16 = 0
 ATTN_F32 = 1
+ATTN_F16 = 2
 
 
 class AttnError(RuntimeError):
@@ -56,15 +57,15 @@ def load_library():
         lib.attn_prefill_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          c_float, c_int, c_float, c_void_p, c_void_p]
-        lib.attn_prefill_fwd_masked.restype = c_int
-        lib.attn_prefill_fwd_masked.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_void_p,
-                                                c_int, c_int, c_int, c_int, c_int, c_int, c_int,
-                                                c_float, c_int, c_float, c_void_p,
-                                                c_void_p, c_int, c_int, ctypes.c_int64, c_float, c_void_p]
+        lib.attn_prefill_fwd_ex.restype = c_int
+        lib.attn_prefill_fwd_ex.argtypes = [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p, c_int, c_void_p,
+                                            c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                            c_float, c_int, c_float, c_void_p,
+                                            c_void_p, c_int, c_int, ctypes.c_int64, c_float, c_void_p]
         lib.attn_decode_workspace_bytes.restype = c_size_t
         lib.attn_decode_workspace_bytes.argtypes = [c_int] * 7
         lib.attn_decode_fwd.restype = c_int
-        lib.attn_decode_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+        lib.attn_decode_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int,
                                         c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                         c_float, c_int, c_float, c_void_p,
                                         c_void_p, c_int, c_int, c_void_p,
@@ -111,8 +112,8 @@ def _row_ptr(t, name):
     import torch
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be a GPU tensor" % name)
-    if t.dtype != torch.bfloat16:
-        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be bfloat16" % name)
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be bfloat16 or float16" % name)
     if t.dim() != 2 or t.stride(1) != 1:
         raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be [rows, width] with contiguous rows" % name)
     return ctypes.c_void_p(t.data_ptr())
@@ -133,6 +134,22 @@ def _odtype(o):
     raise AttnError(ATTN_ERR_INVALID_ARG, "o must be bfloat16 or float32")
 
 
+def _qdtype(q):
+    import torch
+    codes = {torch.bfloat16: ATTN_BF16, torch.float32: ATTN_F32, torch.float16: ATTN_F16}
+    if q.dtype not in codes:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "q must be bfloat16, float16 or float32")
+    return codes[q.dtype]
+
+
+def _kvdtype(*ts):
+    import torch
+    codes = {torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
+    if any(t.dtype != ts[0].dtype for t in ts) or ts[0].dtype not in codes:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "K and V must both be bfloat16 or both float16")
+    return codes[ts[0].dtype]
+
+
 def attn_prefill_fwd(q, k, v, o, lse=None, *, scale, causal=False, softcap=0.0, sinks=None, stream=None):
     """q [B,Sq,Hq,dk], k [B,Sk,Hkv,dk], v [B,Sk,Hkv,dv] bf16; o [B,Sq,Hq,dv] bf16|fp32;
     lse optional fp32 [B,Hq,Sq]; sinks optional fp32 [Hq]. Enqueued on `stream`
@@ -150,25 +167,30 @@ def attn_prefill_fwd(q, k, v, o, lse=None, *, scale, causal=False, softcap=0.0, 
     _check(st)
 
 
-def attn_prefill_fwd_masked(q, k, v, o, mask, lse=None, *, scale, causal=False, softcap=0.0, sinks=None,
-                            max_bias=0.0, stream=None):
-    """attn_prefill_fwd plus an additive fp16 mask [MB, MH, Sq, W] (contiguous, W >= Sk and a
-    multiple of 4; entry [b % MB, h % MH] applies to batch b, head h) times the head's ALiBi
-    slope for max_bias."""
+def attn_prefill_fwd_ex(q, k, v, o, lse=None, *, scale, causal=False, softcap=0.0, sinks=None, mask=None,
+                        max_bias=0.0, stream=None):
+    """attn_prefill_fwd with q in bf16 / fp16 / fp32 and k, v in bf16 / fp16 (taken from the
+    tensors' dtypes), and an optional additive fp16 mask [MB, MH, Sq, W] (contiguous, W >= Sk
+    and a multiple of 4; entry [b % MB, h % MH] applies to batch b, head h) times the head's
+    ALiBi slope for max_bias."""
     import torch
     lib = load_library()
     B, Sq, Hq, dk = q.shape
     _, Sk, Hkv, _ = k.shape
     dv = v.shape[3]
-    if mask.dim() != 4 or mask.shape[2] != Sq:
-        raise AttnError(ATTN_ERR_INVALID_ARG, "mask must be [MB, MH, Sq, W] (got %s)" % (tuple(mask.shape),))
-    st = lib.attn_prefill_fwd_masked(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
-                                     _ptr(v, "v", torch.bfloat16), _ptr(o, "o"), _odtype(o),
-                                     _ptr(lse, "lse", torch.float32, True),
-                                     B, Hq, Hkv, Sq, Sk, dk, dv, float(scale), int(bool(causal)), float(softcap),
-                                     _ptr(sinks, "sinks", torch.float32, True),
-                                     _ptr(mask, "mask", torch.float16), int(mask.shape[0]), int(mask.shape[1]),
-                                     int(mask.shape[3]), float(max_bias), _stream(stream))
+    mb = mh = 1
+    ms = 0
+    if mask is not None:
+        if mask.dim() != 4 or mask.shape[2] != Sq:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "mask must be [MB, MH, Sq, W] (got %s)" % (tuple(mask.shape),))
+        mb, mh, ms = int(mask.shape[0]), int(mask.shape[1]), int(mask.shape[3])
+    kvt = _kvdtype(k, v)
+    st = lib.attn_prefill_fwd_ex(_ptr(q, "q"), _qdtype(q), _ptr(k, "k"), _ptr(v, "v"), kvt,
+                                 _ptr(o, "o"), _odtype(o), _ptr(lse, "lse", torch.float32, True),
+                                 B, Hq, Hkv, Sq, Sk, dk, dv, float(scale), int(bool(causal)), float(softcap),
+                                 _ptr(sinks, "sinks", torch.float32, True),
+                                 _ptr(mask, "mask", torch.float16, True), mb, mh, ms, float(max_bias),
+                                 _stream(stream))
     _check(st)
 
 
@@ -204,7 +226,7 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
         dv = o.shape[3] if dv is None else dv
     ws_bytes = workspace.numel() * workspace.element_size()
     if paged:
-        kp, vp = _ptr(k_cache, "k_cache", torch.bfloat16), _ptr(v_cache, "v_cache", torch.bfloat16)
+        kp, vp = _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
     else:
         kp, vp = _row_ptr(k_cache, "k_cache"), _row_ptr(v_cache, "v_cache")
         if not kv_row_stride:
@@ -221,7 +243,7 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
                 raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur / v_cur need one row per token")
     if paged or k_cur is None:
         kcp, vcp = None, None
-    st = lib.attn_decode_fwd(_ptr(q, "q", torch.bfloat16), kp, vp, _ptr(o, "o"), _odtype(o),
+    st = lib.attn_decode_fwd(_ptr(q, "q"), kp, vp, _ptr(o, "o"), _odtype(o), _qdtype(q), _kvdtype(k_cache, v_cache),
                              B, Hq, Hkv, Sq, int(Sk_max), dk, dv, float(scale), int(bool(causal)),
                              float(softcap), _ptr(sinks, "sinks", torch.float32, True),
                              _ptr(block_table, "block_table", torch.int32, True), bs, max_blocks,

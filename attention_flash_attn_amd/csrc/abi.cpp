@@ -44,6 +44,14 @@ attn_status check_common(int B, int Hq, int Hkv, int Sq, int dk, int dv, float s
     return ATTN_OK;
 }
 
+attn_status check_dtypes(int q_dtype, int kv_dtype) {
+    if (q_dtype != ATTN_BF16 && q_dtype != ATTN_F32 && q_dtype != ATTN_F16)
+        return fail(ATTN_ERR_INVALID_ARG, "q_dtype must be ATTN_BF16, ATTN_F32 or ATTN_F16");
+    if (kv_dtype != ATTN_BF16 && kv_dtype != ATTN_F16)
+        return fail(ATTN_ERR_INVALID_ARG, "kv_dtype must be ATTN_BF16 or ATTN_F16");
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -62,12 +70,15 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
-static attn_status prefill_impl(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
-                                int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale, int causal,
-                                float softcap, const float* sinks, const void* mask, int mask_batch,
-                                int mask_heads, int64_t mask_row_stride, float max_bias, void* stream) {
+static attn_status prefill_impl(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype, void* o,
+                                int o_dtype, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv,
+                                float scale, int causal, float softcap, const float* sinks, const void* mask,
+                                int mask_batch, int mask_heads, int64_t mask_row_stride, float max_bias,
+                                void* stream) {
     if (!q || !k || !v || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k, v and o are required");
     attn_status st = check_common(B, Hq, Hkv, Sq, dk, dv, scale, softcap, o_dtype);
+    if (st != ATTN_OK) return st;
+    st = check_dtypes(q_dtype, kv_dtype);
     if (st != ATTN_OK) return st;
     if (Sk <= 0) return fail(ATTN_ERR_INVALID_ARG, "Sk must be positive (got %d)", Sk);
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -100,6 +111,8 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
     a.lse = lse;
     a.sinks = sinks;
     a.o_f32 = o_dtype == ATTN_F32;
+    a.q_type = q_dtype;
+    a.kv_f16 = kv_dtype == ATTN_F16;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -123,17 +136,17 @@ static attn_status prefill_impl(const void* q, const void* k, const void* v, voi
 attn_status attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
                              int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale, int causal,
                              float softcap, const float* sinks, void* stream) {
-    return prefill_impl(q, k, v, o, o_dtype, lse, B, Hq, Hkv, Sq, Sk, dk, dv, scale, causal, softcap, sinks,
-                        nullptr, 1, 1, 0, 0.f, stream);
+    return prefill_impl(q, ATTN_BF16, k, v, ATTN_BF16, o, o_dtype, lse, B, Hq, Hkv, Sq, Sk, dk, dv, scale, causal,
+                        softcap, sinks, nullptr, 1, 1, 0, 0.f, stream);
 }
 
-attn_status attn_prefill_fwd_masked(const void* q, const void* k, const void* v, void* o, int o_dtype, float* lse,
-                                    int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv, float scale,
-                                    int causal, float softcap, const float* sinks, const void* mask,
-                                    int mask_batch, int mask_heads, int64_t mask_row_stride, float max_bias,
-                                    void* stream) {
-    return prefill_impl(q, k, v, o, o_dtype, lse, B, Hq, Hkv, Sq, Sk, dk, dv, scale, causal, softcap, sinks, mask,
-                        mask_batch, mask_heads, mask_row_stride, max_bias, stream);
+attn_status attn_prefill_fwd_ex(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype, void* o,
+                                int o_dtype, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv,
+                                float scale, int causal, float softcap, const float* sinks, const void* mask,
+                                int mask_batch, int mask_heads, int64_t mask_row_stride, float max_bias,
+                                void* stream) {
+    return prefill_impl(q, q_dtype, k, v, kv_dtype, o, o_dtype, lse, B, Hq, Hkv, Sq, Sk, dk, dv, scale, causal,
+                        softcap, sinks, mask, mask_batch, mask_heads, mask_row_stride, max_bias, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv) {
@@ -141,7 +154,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
     return attn::decode_plan(B, Hq, Hkv, Sq, Sk_max, dk, dv).ws_bytes;
 }
 
-attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype, int B,
+attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype,
+                            int q_dtype, int kv_dtype, int B,
                             int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv, float scale, int causal,
                             float softcap, const float* sinks, const int32_t* block_table, int block_size,
                             int max_blocks_per_seq, const int32_t* seq_lens, const int32_t* row_index,
@@ -150,6 +164,8 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
                             void* stream) {
     if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o are required");
     attn_status st = check_common(B, Hq, Hkv, Sq, dk, dv, scale, softcap, o_dtype);
+    if (st != ATTN_OK) return st;
+    st = check_dtypes(q_dtype, kv_dtype);
     if (st != ATTN_OK) return st;
     const bool paged = block_table != nullptr;
     const bool gathered = row_index != nullptr;
@@ -198,6 +214,8 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
     a.o = o;
     a.sinks = sinks;
     a.o_f32 = o_dtype == ATTN_F32;
+    a.q_type = q_dtype;
+    a.kv_f16 = kv_dtype == ATTN_F16;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;

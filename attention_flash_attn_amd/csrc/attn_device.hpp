@@ -77,6 +77,78 @@ __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
 }
 
+// ---- operand element type: bf16 (F16 = false) or IEEE fp16 (F16 = true) ----
+// 16-bit operands travel as bf16x8 bit patterns and are reinterpreted for the
+// f16 MFMAs (same shapes and rates on gfx950).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Round two floats to the operand type (nearest even) and pack them, low half first.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_op2(float lo, float hi) {
+    if constexpr (F16) {
+        f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        return pack_bf16x2(lo, hi);
+    }
+}
+// acc + lo(w) + hi(w) for a packed pair of the operand type (v_dot2 with ones).
+template <bool F16>
+__device__ __forceinline__ float add_op2(uint32_t w, float acc) {
+    if constexpr (F16) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+    } else {
+        return add_bf16x2(w, acc);
+    }
+}
+
+// Element type of a query tensor: 0 = bf16, 1 = fp32, 2 = fp16 (the ABI's codes).
+// Loads 8 consecutive elements at p (element index `idx`) as the MFMA operand type.
+template <bool F16>
+__device__ __forceinline__ bf16x8 load_q8(const void* p, size_t idx, int qtype) {
+    if (qtype == 1) {
+        const f32x4 a = *(const f32x4*)((const float*)p + idx);
+        const f32x4 b = *(const f32x4*)((const float*)p + idx + 4);
+        const u32x4 w = {pack_op2<F16>(a[0], a[1]), pack_op2<F16>(a[2], a[3]), pack_op2<F16>(b[0], b[1]),
+                         pack_op2<F16>(b[2], b[3])};
+        return __builtin_bit_cast(bf16x8, w);
+    }
+    if (qtype == 2 && !F16) {  // fp16 -> bf16 (read as an fp16 vector and widened element-wise)
+        const f16x8 hv = *(const f16x8*)((const _Float16*)p + idx);
+        const u32x4 w = {pack_op2<F16>((float)hv[0], (float)hv[1]), pack_op2<F16>((float)hv[2], (float)hv[3]),
+                         pack_op2<F16>((float)hv[4], (float)hv[5]), pack_op2<F16>((float)hv[6], (float)hv[7])};
+        return __builtin_bit_cast(bf16x8, w);
+    }
+    const u32x4 raw = *(const u32x4*)((const uint16_t*)p + idx);
+    if (qtype == 0 && F16) {  // bf16 -> fp16
+        const u32x4 w = {pack_op2<F16>(bf16lo_to_f32(raw[0]), bf16hi_to_f32(raw[0])),
+                         pack_op2<F16>(bf16lo_to_f32(raw[1]), bf16hi_to_f32(raw[1])),
+                         pack_op2<F16>(bf16lo_to_f32(raw[2]), bf16hi_to_f32(raw[2])),
+                         pack_op2<F16>(bf16lo_to_f32(raw[3]), bf16hi_to_f32(raw[3]))};
+        return __builtin_bit_cast(bf16x8, w);
+    }
+    return __builtin_bit_cast(bf16x8, raw);  // already the operand type
+}
+
 // Direct HBM -> LDS copy of 16 bytes per lane: lane i writes lds_base + 16 * i
 // (lds_base must be wave-uniform). Inactive lanes write nothing.
 __device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {

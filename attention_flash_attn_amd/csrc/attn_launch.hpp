@@ -15,6 +15,8 @@ struct PrefillArgs {
     float* lse;
     const float* sinks;
     int o_f32;
+    int q_type = 0;  // 0 bf16, 1 fp32, 2 fp16
+    int kv_f16 = 0;  // K and V are fp16 (else bf16)
     int B, Hq, Hkv, Sq, Sk, dk, dv;
     float scale;
     int causal;
@@ -37,6 +39,8 @@ struct DecodeArgs {
     void* o;
     const float* sinks;
     int o_f32;
+    int q_type = 0;  // 0 bf16, 1 fp32, 2 fp16
+    int kv_f16 = 0;  // K and V are fp16 (else bf16)
     int B, Hq, Hkv, Sq, Sk_max, dk, dv;
     float scale;
     int causal;

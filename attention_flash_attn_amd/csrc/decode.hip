@@ -24,7 +24,7 @@ namespace attn {
 namespace {
 
 struct SplitParams {
-    const uint16_t* __restrict__ q;
+    const void* __restrict__ q;  // bf16, fp32 or fp16 (q_type)
     const uint16_t* __restrict__ kc;
     const uint16_t* __restrict__ vc;
     float* __restrict__ ws_o;   // [rows][n_split][dv]
@@ -32,10 +32,11 @@ struct SplitParams {
     const int32_t* __restrict__ block_table;
     const int32_t* __restrict__ seq_lens;
     int B, Hq, Hkv, Sq, group, nq, bs_log2, max_blocks;
-    int ncg;  // groups of 32 query columns per KV head (one workgroup each)
+    int ncg;  // groups of 16 * CB query columns per KV head (one workgroup each)
     int n_split, split_len;
     float c_score, c_tanh, c_cap;
     int causal, softcap_on;
+    int q_type;  // 0 bf16, 1 fp32, 2 fp16
 };
 
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units), as in the prefill kernel
@@ -46,7 +47,8 @@ constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units), as in the p
 // K fragments go HBM -> registers one step ahead; V rows go HBM -> LDS (one
 // 1 KB direct load per instruction) one step ahead into a per-wave double
 // buffer, for the transposing read of the V^T operand.
-template <int DK, int DV, int CB>
+// F16: the caches (and the MFMA operands, P included) are IEEE fp16 instead of bf16.
+template <int DK, int DV, int CB, bool F16>
 __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
     constexpr int DKP = DK < 32 ? 32 : DK;  // QK k-steps of 32 (zero-padded)
     constexpr int KQ = DKP / 32;
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
     const int lane = threadIdx.x, grp = lane >> 4, c16 = lane & 15;
     // split-major grid: every (KV head, sequence) pair of split 0 first, then split 1, ...,
     // so the last work dispatched belongs to the longest sequences' final (often partial) splits
-    const int split = blockIdx.z, g = blockIdx.x / p.ncg, cg0 = (blockIdx.x % p.ncg) * 32, b = blockIdx.y;
+    const int split = blockIdx.z, g = blockIdx.x / p.ncg, cg0 = (blockIdx.x % p.ncg) * (16 * CB), b = blockIdx.y;
     const int L = p.seq_lens[b];
     const int start = split * p.split_len;
     if (start >= L) return;  // the combine pass only reads splits that start below L
@@ -82,13 +84,12 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
         const bool ok = colq < p.nq;
         const int si = ok ? colq / p.group : 0;
         const int h = g * p.group + (ok ? colq % p.group : 0);
-        const uint16_t* qrow = p.q + ((size_t)(b * p.Sq + si) * p.Hq + h) * DK;
+        const size_t qrow = ((size_t)(b * p.Sq + si) * p.Hq + h) * DK;
 #pragma unroll
         for (int kk = 0; kk < KQ; ++kk) {
             const int dk0 = kk * 32 + grp * 8;
-            u32x4 w = {0, 0, 0, 0};
-            if (ok && dk0 < DK) w = *(const u32x4*)(qrow + dk0);
-            qf[cb][kk] = __builtin_bit_cast(bf16x8, w);
+            qf[cb][kk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+            if (ok && dk0 < DK) qf[cb][kk] = load_q8<F16>(p.q, qrow + dk0, p.q_type);
         }
         lim[cb] = min(end - 1, p.causal ? L - p.Sq + si : L - 1);  // last key this column may see
     }
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
                 sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KQ; ++kk)
-                    sacc[kb] = mfma16x16x32(__builtin_bit_cast(bf16x8, kc_[kb][kk]), qf[cb][kk], sacc[kb]);
+                    sacc[kb] = mma16<F16>(__builtin_bit_cast(bf16x8, kc_[kb][kk]), qf[cb][kk], sacc[kb]);
             }
             float mx = -INFINITY;
 #pragma unroll
@@ -194,11 +195,11 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
             uint32_t pk[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                pk[2 * kb] = pack_bf16x2(exp2_fast(sacc[kb][0] + nm), exp2_fast(sacc[kb][1] + nm));
-                pk[2 * kb + 1] = pack_bf16x2(exp2_fast(sacc[kb][2] + nm), exp2_fast(sacc[kb][3] + nm));
+                pk[2 * kb] = pack_op2<F16>(exp2_fast(sacc[kb][0] + nm), exp2_fast(sacc[kb][1] + nm));
+                pk[2 * kb + 1] = pack_op2<F16>(exp2_fast(sacc[kb][2] + nm), exp2_fast(sacc[kb][3] + nm));
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) l_run[cb] = add_bf16x2(pk[j], l_run[cb]);
+            for (int j = 0; j < 4; ++j) l_run[cb] = add_op2<F16>(pk[j], l_run[cb]);
             const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
             // O^T += V^T P^T: V^T rows are keys grp*4 + 0..3 (block 0) and 16 + grp*4 + 0..3 (block 1)
             const int ra = grp * 4 + (c16 >> 2);
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
                 const int ch = dc >> 3, within = (dc & 7) * 2;
                 const bf16x4 va = lds_read_tr16(vt + ra * VROW + ((ch ^ swz<NCV, true>(ra)) * 16) + within);
                 const bf16x4 vb = lds_read_tr16(vt + rb * VROW + ((ch ^ swz<NCV, true>(rb)) * 16) + within);
-                oacc[cb][d] = mfma16x16x32(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[cb][d]);
+                oacc[cb][d] = mma16<F16>(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[cb][d]);
             }
         }
     };
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
 //   K operand: a 128-bit read of one chunk by 16 consecutive rows;
 //   V^T operand: a transposing read of 4 consecutive rows x 32 bytes.
 struct GatherParams {
-    const uint16_t* __restrict__ q;
+    const void* __restrict__ q;  // bf16, fp32 or fp16 (q_type)
     const uint16_t* __restrict__ kc;
     const uint16_t* __restrict__ vc;
     float* __restrict__ ws_o;
@@ -302,6 +303,7 @@ struct GatherParams {
     long long row_stride;  // elements
     float c_score, c_tanh, c_cap;
     int causal, softcap_on;
+    int q_type;
 };
 
 // keys per split the LDS index table holds: a split of up to 1024 selected keys, plus the
@@ -326,7 +328,7 @@ __device__ __forceinline__ void wait_stages(int later) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int DK, int DV, int NW, bool VK>
+template <int DK, int DV, int NW, bool VK, bool F16>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_gathered_split_kernel(GatherParams p) {
     constexpr int NT = NW * 64;
@@ -370,12 +372,11 @@ void decode_gathered_split_kernel(GatherParams p) {
     const bool hok = h < p.Hq;
     bf16x8 qf[KQ];
     {
-        const uint16_t* qrow = p.q + ((size_t)t * p.Hq + (hok ? h : 0)) * DK;
+        const size_t qrow = ((size_t)t * p.Hq + (hok ? h : 0)) * DK;
 #pragma unroll
         for (int kk = 0; kk < KQ; ++kk) {
-            u32x4 w = {0, 0, 0, 0};
-            if (hok) w = *(const u32x4*)(qrow + kk * 32 + grp * 8);
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
+            qf[kk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+            if (hok) qf[kk] = load_q8<F16>(p.q, qrow + kk * 32 + grp * 8, p.q_type);
         }
     }
 
@@ -452,7 +453,7 @@ void decode_gathered_split_kernel(GatherParams p) {
             const bf16x8 a = kring[idx % PFK];
             if (idx + PFK < NQK) kring[idx % PFK] = kload(idx + PFK);
             const int kk = idx >> 1, kb = idx & 1;
-            sacc[kb][kk & 1] = mfma16x16x32(a, qf[kk], sacc[kb][kk & 1]);
+            sacc[kb][kk & 1] = mma16<F16>(a, qf[kk], sacc[kb][kk & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         f32x4 sc[2];
@@ -489,11 +490,11 @@ void decode_gathered_split_kernel(GatherParams p) {
         uint32_t pk[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            pk[2 * kb] = pack_bf16x2(exp2_fast(sc[kb][0] + nm), exp2_fast(sc[kb][1] + nm));
-            pk[2 * kb + 1] = pack_bf16x2(exp2_fast(sc[kb][2] + nm), exp2_fast(sc[kb][3] + nm));
+            pk[2 * kb] = pack_op2<F16>(exp2_fast(sc[kb][0] + nm), exp2_fast(sc[kb][1] + nm));
+            pk[2 * kb + 1] = pack_op2<F16>(exp2_fast(sc[kb][2] + nm), exp2_fast(sc[kb][3] + nm));
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) l_run = add_bf16x2(pk[j], l_run);
+        for (int j = 0; j < 4; ++j) l_run = add_op2<F16>(pk[j], l_run);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
 
         constexpr int PFV = DBV < ATTN_GPF_V ? DBV : ATTN_GPF_V;
@@ -510,7 +511,7 @@ void decode_gathered_split_kernel(GatherParams p) {
         for (int d = 0; d < DBV; ++d) {
             const bf16x8 a = vring[d % PFV];
             if (d + PFV < DBV) vring[d % PFV] = vload(d + PFV);
-            oacc[d] = mfma16x16x32(a, pb, oacc[d]);
+            oacc[d] = mma16<F16>(a, pb, oacc[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -617,13 +618,21 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
     }
 }
 
-template <int DK, int DV>
-hipError_t launch_paged(const SplitParams& sp, dim3 grid, hipStream_t stream) {
-    if (sp.nq <= 16)  // one group of up to 16 columns; otherwise groups of 32
-        hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 1>), grid, dim3(64), 0, stream, sp);
-    else
-        hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 2>), grid, dim3(64), 0, stream, sp);
+// Query columns per workgroup: 16 (one MFMA block) at head dims >= 192, whose registers
+// are full, else up to 32; more columns take more workgroups.
+inline int paged_cols(int dk, int nq) { return (dk >= 192 || nq <= 16) ? 16 : 32; }
+
+template <int DK, int DV, bool F16>
+hipError_t launch_paged_t(const SplitParams& sp, dim3 grid, hipStream_t stream) {
+    if (paged_cols(DK, sp.nq) == 16)
+        hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 1, F16>), grid, dim3(64), 0, stream, sp);
+    else if constexpr (DK < 192)
+        hipLaunchKernelGGL((decode_paged_split_kernel<DK, DV, 2, F16>), grid, dim3(64), 0, stream, sp);
     return hipGetLastError();
+}
+template <int DK, int DV>
+hipError_t launch_paged(const SplitParams& sp, bool f16, dim3 grid, hipStream_t stream) {
+    return f16 ? launch_paged_t<DK, DV, true>(sp, grid, stream) : launch_paged_t<DK, DV, false>(sp, grid, stream);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, const DecodePlan& pl, float* ws_o, float* ws_ml,
@@ -689,7 +698,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     const float kLog2eH = 1.4426950408889634f;
 
     SplitParams sp;
-    sp.q = (const uint16_t*)a.q;
+    sp.q = a.q;
+    sp.q_type = a.q_type;
     sp.kc = (const uint16_t*)a.k_cache;
     sp.vc = (const uint16_t*)a.v_cache;
     sp.ws_o = ws_o;
@@ -702,7 +712,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     sp.Sq = a.Sq;
     sp.group = a.Hq / a.Hkv;
     sp.nq = a.Sq * sp.group;
-    sp.ncg = (sp.nq + 31) / 32;
+    const int cols = paged_cols(a.dk, sp.nq);
+    sp.ncg = (sp.nq + cols - 1) / cols;
     int lg = 0;
     while ((1 << lg) < a.block_size) ++lg;
     sp.bs_log2 = lg;
@@ -718,7 +729,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     hipError_t e;
     if (a.row_index != nullptr) {
         GatherParams gp;
-        gp.q = (const uint16_t*)a.q;
+        gp.q = a.q;
+        gp.q_type = a.q_type;
         gp.kc = (const uint16_t*)a.k_cache;
         gp.vc = (const uint16_t*)a.v_cache;
         gp.ws_o = ws_o;
@@ -742,24 +754,36 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         gp.softcap_on = sp.softcap_on;
         constexpr int NW = 4;
         const dim3 ggrid((unsigned)pl.n_split, (unsigned)((a.Hq + NW * 16 - 1) / (NW * 16)), (unsigned)a.B);
-        if (a.v_cache == a.k_cache)
-            hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, true>), ggrid, dim3(NW * 64), 0, stream, gp);
-        else
-            hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, false>), ggrid, dim3(NW * 64), 0, stream, gp);
+        const bool vk = a.v_cache == a.k_cache;
+        if (a.kv_f16) {
+            if (vk)
+                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, true, true>), ggrid, dim3(NW * 64), 0,
+                                   stream, gp);
+            else
+                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, false, true>), ggrid, dim3(NW * 64), 0,
+                                   stream, gp);
+        } else {
+            if (vk)
+                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, true, false>), ggrid, dim3(NW * 64), 0,
+                                   stream, gp);
+            else
+                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, false, false>), ggrid, dim3(NW * 64), 0,
+                                   stream, gp);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         return launch_combine(a, pl, ws_o, ws_ml, nullptr, stream);
     }
     const dim3 grid((unsigned)(a.Hkv * sp.ncg), (unsigned)a.B, (unsigned)pl.n_split);
     switch (a.dk * 1000 + a.dv) {
-        case 16016: e = launch_paged<16, 16>(sp, grid, stream); break;
-        case 32032: e = launch_paged<32, 32>(sp, grid, stream); break;
-        case 64064: e = launch_paged<64, 64>(sp, grid, stream); break;
-        case 96096: e = launch_paged<96, 96>(sp, grid, stream); break;
-        case 128128: e = launch_paged<128, 128>(sp, grid, stream); break;
-        case 192192: e = launch_paged<192, 192>(sp, grid, stream); break;
-        case 256256: e = launch_paged<256, 256>(sp, grid, stream); break;
-        case 192128: e = launch_paged<192, 128>(sp, grid, stream); break;
+        case 16016: e = launch_paged<16, 16>(sp, a.kv_f16 != 0, grid, stream); break;
+        case 32032: e = launch_paged<32, 32>(sp, a.kv_f16 != 0, grid, stream); break;
+        case 64064: e = launch_paged<64, 64>(sp, a.kv_f16 != 0, grid, stream); break;
+        case 96096: e = launch_paged<96, 96>(sp, a.kv_f16 != 0, grid, stream); break;
+        case 128128: e = launch_paged<128, 128>(sp, a.kv_f16 != 0, grid, stream); break;
+        case 192192: e = launch_paged<192, 192>(sp, a.kv_f16 != 0, grid, stream); break;
+        case 256256: e = launch_paged<256, 256>(sp, a.kv_f16 != 0, grid, stream); break;
+        case 192128: e = launch_paged<192, 128>(sp, a.kv_f16 != 0, grid, stream); break;
         default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -48,7 +48,7 @@ namespace attn {
 namespace {
 
 struct PrefillParams {
-    const uint16_t* __restrict__ q;
+    const void* __restrict__ q;  // bf16, fp32 or fp16 (q_type), converted to the operand type at load
     const uint16_t* __restrict__ k;
     const uint16_t* __restrict__ v;
     void* __restrict__ o;
@@ -65,6 +65,7 @@ struct PrefillParams {
     int mask_batch, mask_heads;
     float max_bias;
     int n_head_log2;
+    int q_type;  // 0 bf16, 1 fp32, 2 fp16
 };
 
 // 8-byte buffer load (4 fp16 mask entries); offsets past the resource read 0.
@@ -90,7 +91,8 @@ constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 #define ATTN_D256_CFG 32, 8, 2
 #endif
 
-template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool ADDM, bool OF32>
+// F16: K, V (and the MFMA operands, P included) are IEEE fp16 instead of bf16.
+template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool ADDM, bool F16, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillParams p) {
     constexpr bool LOG2 = SOFTCAP || ADDM;  // scores converted to log2 units before the max
@@ -200,12 +202,11 @@ void prefill_kernel(PrefillParams p) {
     // this lane's Q fragments: row qi, chunks 2*kk + half
     bf16x8 qf[KK];
     {
-        const uint16_t* qrow = p.q + ((size_t)(b * p.Sq + qi) * p.Hq + h) * DK;
+        const size_t qrow = ((size_t)(b * p.Sq + qi) * p.Hq + h) * DK;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            u32x4 w = {0, 0, 0, 0};
-            if (qi < p.Sq) w = *(const u32x4*)(qrow + (2 * kk + half) * 8);
-            qf[kk] = __builtin_bit_cast(bf16x8, w);
+            qf[kk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+            if (qi < p.Sq) qf[kk] = load_q8<F16>(p.q, qrow + (2 * kk + half) * 8, p.q_type);
         }
     }
 
@@ -273,7 +274,7 @@ void prefill_kernel(PrefillParams p) {
         for (int idx = 0; idx < NQK; ++idx) {
             const bf16x8 a = kring[idx % PFK];
             if (idx + PFK < NQK) kring[idx % PFK] = kload(idx + PFK);
-            sacc[idx / KK] = mfma32x32x16(a, qf[idx % KK], sacc[idx / KK]);
+            sacc[idx / KK] = mma32<F16>(a, qf[idx % KK], sacc[idx / KK]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // scores in log2 units (softcap) or raw (scaled inside the exponent), mask, tile max
@@ -343,8 +344,8 @@ void prefill_kernel(PrefillParams p) {
             for (int j = 0; j < 8; ++j) {
                 const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][2 * j], cs, nm));
                 const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][2 * j + 1], cs, nm));
-                pk[kb][j] = pack_bf16x2(p0, p1);
-                l_run = add_bf16x2(pk[kb][j], l_run);
+                pk[kb][j] = pack_op2<F16>(p0, p1);
+                l_run = add_op2<F16>(pk[kb][j], l_run);
             }
         }
         // O^T += V^T P^T, 16 keys per MFMA; V^T fragments read PF steps ahead
@@ -366,7 +367,7 @@ void prefill_kernel(PrefillParams p) {
             const bf16x8 a = vring[idx % PFV];
             if (idx + PFV < NPV) vring[idx % PFV] = vload(idx + PFV);
             const u32x4 pw = {pk[kb][4 * jj], pk[kb][4 * jj + 1], pk[kb][4 * jj + 2], pk[kb][4 * jj + 3]};
-            oacc[d] = mfma32x32x16(a, __builtin_bit_cast(bf16x8, pw), oacc[d]);
+            oacc[d] = mma32<F16>(a, __builtin_bit_cast(bf16x8, pw), oacc[d]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -444,35 +445,41 @@ void prefill_kernel(PrefillParams p) {
     }
 }
 
-template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool ADDM>
+template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool ADDM, bool F16>
 hipError_t launch_variant(PrefillParams p, bool of32, hipStream_t stream) {
     constexpr int BM = NW * 32;
     p.nqt = (p.Sq + BM - 1) / BM;
     const dim3 grid((unsigned)(p.nqt * p.Hq * p.B)), block(NW * 64);
     if (of32)
-        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, ADDM, true>), grid, block, 0, stream,
-                           p);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, ADDM, F16, true>), grid, block, 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, ADDM, false>), grid, block, 0, stream,
-                           p);
+        hipLaunchKernelGGL((prefill_kernel<DK, DV, BN, NW, OCC, CAUSAL, SOFTCAP, ADDM, F16, false>), grid, block, 0,
+                           stream, p);
     return hipGetLastError();
 }
 
-template <int DK, int DV, int BN, int NW, int OCC, bool ADDM>
+template <int DK, int DV, int BN, int NW, int OCC, bool ADDM, bool F16>
 hipError_t launch_flags(const PrefillParams& p, bool causal, bool softcap, bool of32, hipStream_t stream) {
     if (causal) {
-        return softcap ? launch_variant<DK, DV, BN, NW, OCC, true, true, ADDM>(p, of32, stream)
-                       : launch_variant<DK, DV, BN, NW, OCC, true, false, ADDM>(p, of32, stream);
+        return softcap ? launch_variant<DK, DV, BN, NW, OCC, true, true, ADDM, F16>(p, of32, stream)
+                       : launch_variant<DK, DV, BN, NW, OCC, true, false, ADDM, F16>(p, of32, stream);
     }
-    return softcap ? launch_variant<DK, DV, BN, NW, OCC, false, true, ADDM>(p, of32, stream)
-                   : launch_variant<DK, DV, BN, NW, OCC, false, false, ADDM>(p, of32, stream);
+    return softcap ? launch_variant<DK, DV, BN, NW, OCC, false, true, ADDM, F16>(p, of32, stream)
+                   : launch_variant<DK, DV, BN, NW, OCC, false, false, ADDM, F16>(p, of32, stream);
 }
 
 // (BN, NW, OCC) without a mask; (BNM, NWM, OCCM) with one
 template <int DK, int DV, int BN, int NW, int OCC, int BNM = BN, int NWM = NW, int OCCM = OCC>
-hipError_t launch_inst(const PrefillParams& p, bool causal, bool softcap, bool of32, hipStream_t stream) {
-    if (p.mask != nullptr) return launch_flags<DK, DV, BNM, NWM, OCCM, true>(p, causal, softcap, of32, stream);
-    return launch_flags<DK, DV, BN, NW, OCC, false>(p, causal, softcap, of32, stream);
+hipError_t launch_inst(const PrefillParams& p, bool kv_f16, bool causal, bool softcap, bool of32,
+                       hipStream_t stream) {
+    if (kv_f16) {
+        if (p.mask != nullptr)
+            return launch_flags<DK, DV, BNM, NWM, OCCM, true, true>(p, causal, softcap, of32, stream);
+        return launch_flags<DK, DV, BN, NW, OCC, false, true>(p, causal, softcap, of32, stream);
+    }
+    if (p.mask != nullptr) return launch_flags<DK, DV, BNM, NWM, OCCM, true, false>(p, causal, softcap, of32, stream);
+    return launch_flags<DK, DV, BN, NW, OCC, false, false>(p, causal, softcap, of32, stream);
 }
 
 }  // namespace
@@ -489,7 +496,8 @@ bool prefill_supported(int dk, int dv) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     PrefillParams p;
-    p.q = (const uint16_t*)a.q;
+    p.q = a.q;
+    p.q_type = a.q_type;
     p.k = (const uint16_t*)a.k;
     p.v = (const uint16_t*)a.v;
     p.o = a.o;
@@ -515,16 +523,16 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     int nl2 = 1;
     while (nl2 * 2 <= a.Hq) nl2 *= 2;
     p.n_head_log2 = nl2;
-    const bool of32 = a.o_f32 != 0, causal = a.causal != 0;
+    const bool of32 = a.o_f32 != 0, causal = a.causal != 0, kv_f16 = a.kv_f16 != 0;
     switch (a.dk * 1000 + a.dv) {
-        case 16016: return launch_inst<16, 16, 64, 4, 2>(p, causal, softcap, of32, stream);
-        case 32032: return launch_inst<32, 32, 64, 4, 2>(p, causal, softcap, of32, stream);
-        case 64064: return launch_inst<64, 64, 64, 4, 2>(p, causal, softcap, of32, stream);
-        case 96096: return launch_inst<96, 96, 64, 4, 2>(p, causal, softcap, of32, stream);
-        case 128128: return launch_inst<128, 128, ATTN_D128_CFG>(p, causal, softcap, of32, stream);
-        case 192192: return launch_inst<192, 192, 32, 4, 2>(p, causal, softcap, of32, stream);
-        case 256256: return launch_inst<256, 256, ATTN_D256_CFG, 32, 4, 1>(p, causal, softcap, of32, stream);
-        case 192128: return launch_inst<192, 128, 32, 4, 2>(p, causal, softcap, of32, stream);
+        case 16016: return launch_inst<16, 16, 64, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
+        case 32032: return launch_inst<32, 32, 64, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
+        case 64064: return launch_inst<64, 64, 64, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
+        case 96096: return launch_inst<96, 96, 64, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
+        case 128128: return launch_inst<128, 128, ATTN_D128_CFG>(p, kv_f16, causal, softcap, of32, stream);
+        case 192192: return launch_inst<192, 192, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
+        case 256256: return launch_inst<256, 256, ATTN_D256_CFG, 32, 4, 1>(p, kv_f16, causal, softcap, of32, stream);
+        case 192128: return launch_inst<192, 128, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -81,6 +81,28 @@ def normal_bf16(seed, tag, shape, std=1.0, chunk=1 << 22, threads=None):
     return out.reshape(shape)
 
 
+def normal_typed(seed, tag, shape, dtype, std=1.0):
+    """The same N(0, std^2) fp32 draws as normal_bf16, in the element type `dtype`:
+    "bf16" (bit patterns, uint16), "f16" (numpy float16, round to nearest even) or
+    "f32" (unrounded)."""
+    if dtype == "bf16":
+        return normal_bf16(seed, tag, shape, std)
+    n = int(np.prod(shape)) if len(shape) else 1
+    x = np.empty(n, dtype=np.float32)
+    for i, s in enumerate(range(0, n, 1 << 22)):
+        e = min(n, s + (1 << 22))
+        r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(tag), i])))
+        x[s:e] = r.standard_normal(e - s, dtype=np.float32)
+        if std != 1.0:
+            x[s:e] *= np.float32(std)
+    x = x.reshape(shape)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "f32":
+        return x
+    raise ValueError(dtype)
+
+
 def prefill_case(seed, B, Sq, Sk, Hq, Hkv, dk, dv, std=1.0, sinks=False):
     """Dense prefill inputs: q [B,Sq,Hq,dk], k [B,Sk,Hkv,dk], v [B,Sk,Hkv,dv] bf16 bits; sinks [Hq] fp32 or None."""
     rng = np.random.Generator(np.random.PCG64(seed))

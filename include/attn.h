@@ -5,7 +5,7 @@
  *
  *     x_j  = scale * <q_i, k_j>                  raw dot product, scaled afterwards
  *     x_j  = softcap * tanh(x_j / softcap)       only when softcap != 0
- *     x_j += slope_h * mask[i, j]                only with an additive mask (attn_prefill_fwd_masked)
+ *     x_j += slope_h * mask[i, j]                only with an additive mask (attn_prefill_fwd_ex)
  *     keys excluded by the mask are dropped
  *     o_i  = sum_j e^{x_j} v_j / (sum_j e^{x_j} + e^{sink_h})     (sink term only with sinks)
  *
@@ -25,7 +25,14 @@
  *     call path: it validates on the host, enqueues kernels on `stream` and
  *     returns. Outputs are valid once the stream has executed the work.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
- *   - bf16 tensors are IEEE bfloat16 bit patterns; fp32 is IEEE binary32.
+ *   - bf16 tensors are IEEE bfloat16 bit patterns; fp32 is IEEE binary32;
+ *     fp16 is IEEE binary16.
+ *   - Operand types (the _ex entry point and attn_decode_fwd): K and V are
+ *     bf16 or fp16 (kv_dtype); Q is bf16, fp16 or fp32 (q_dtype) and is
+ *     rounded (nearest even) to the K/V type on load, since both products run
+ *     on 16-bit MFMAs with fp32 accumulation (the fa.metal tensor kernel on the
+ *     "ggml-metal: FA tensor path" page takes fp16 K/V with an fp32 Q). The
+ *     probabilities feed the second product in the K/V type as well.
  *   - All argument checks run before any HIP call. On an error status nothing
  *     has been enqueued and the outputs are untouched (ATTN_ERR_HIP: a launch
  *     failed; outputs are then undefined). attn_last_error() gives a message.
@@ -64,7 +71,8 @@ typedef enum attn_status {
 
 typedef enum attn_dtype {
     ATTN_BF16 = 0,
-    ATTN_F32 = 1
+    ATTN_F32 = 1,
+    ATTN_F16 = 2     /* IEEE binary16 */
 } attn_dtype;
 
 /* ATTN_ABI_VERSION of the built library. */
@@ -96,30 +104,33 @@ attn_status attn_prefill_fwd(const void* q, const void* k, const void* v,
                              void* stream);
 
 /*
- * Prefill with an additive mask and optional ALiBi slopes (the mask and
- * max_bias arguments of the fa.metal tensor kernel on the "ggml-metal: FA
- * tensor path" page: the mask entry, times the head's slope, is added to the
- * score after the softcap). Arguments as attn_prefill_fwd, plus:
+ * General prefill: operand types, an additive mask and ALiBi slopes (the
+ * mask and max_bias arguments of the fa.metal tensor kernel on the
+ * "ggml-metal: FA tensor path" page: the mask entry, times the head's slope,
+ * is added to the score after the softcap). Arguments as attn_prefill_fwd, plus:
+ *   q_dtype  ATTN_BF16, ATTN_F16 or ATTN_F32 (q is then [B, Sq, Hq, dk] of that type)
+ *   kv_dtype ATTN_BF16 or ATTN_F16 (k and v of that type)
  *   mask  IEEE fp16 [mask_batch, mask_heads, Sq, mask_row_stride], contiguous,
  *         16-byte aligned; entry [b % mask_batch, h % mask_heads, i, j] is added
  *         for query i, key j of batch b and query head h (columns j >= Sk are
- *         ignored). -inf drops the key. NULL = no mask (then this call is
- *         attn_prefill_fwd; max_bias has nothing to scale).
+ *         ignored). -inf drops the key. NULL = no mask (max_bias then has
+ *         nothing to scale).
  *   mask_batch, mask_heads >= 1 (1 = shared by all batch entries / heads).
  *   mask_row_stride >= Sk, a multiple of 4 (elements between query rows);
  *         one [Sq, mask_row_stride] slab must be under 4 GiB.
  *   max_bias >= 0: ALiBi. Head h's slope is m0^(h+1) for h < n, else
  *         m1^(2(h - n) + 1), with n the largest power of two <= Hq,
  *         m0 = 2^(-max_bias / n), m1 = 2^(-max_bias / (2n)); 0 gives slope 1.
- * causal may be combined with the mask (both apply).
+ * causal may be combined with the mask (both apply). attn_prefill_fwd is this
+ * call with bf16 Q, K, V and no mask.
  */
-attn_status attn_prefill_fwd_masked(const void* q, const void* k, const void* v,
-                                    void* o, int o_dtype, float* lse,
-                                    int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv,
-                                    float scale, int causal, float softcap, const float* sinks,
-                                    const void* mask, int mask_batch, int mask_heads,
-                                    int64_t mask_row_stride, float max_bias,
-                                    void* stream);
+attn_status attn_prefill_fwd_ex(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                                void* o, int o_dtype, float* lse,
+                                int B, int Hq, int Hkv, int Sq, int Sk, int dk, int dv,
+                                float scale, int causal, float softcap, const float* sinks,
+                                const void* mask, int mask_batch, int mask_heads,
+                                int64_t mask_row_stride, float max_bias,
+                                void* stream);
 
 /*
  * Workspace (bytes) that attn_decode_fwd needs for these sizes: the split-KV
@@ -137,10 +148,11 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  * attn_decode_workspace_bytes; B and the number of ranges must not exceed
  * 65535 (ATTN_ERR_UNSUPPORTED otherwise).
  *
- *   q   bf16 [B, Sq, Hq, dk] contiguous;   o [B, Sq, Hq, dv] of type o_dtype.
+ *   q   [B, Sq, Hq, dk] contiguous, of type q_dtype (bf16, fp16 or fp32);
+ *   caches of type kv_dtype (bf16 or fp16);   o [B, Sq, Hq, dv] of type o_dtype.
  *
  * Paged mode (block_table != NULL, row_index == NULL):
- *   k_cache bf16 [n_blocks, Hkv, block_size, dk], v_cache bf16 [n_blocks, Hkv, block_size, dv]
+ *   k_cache [n_blocks, Hkv, block_size, dk], v_cache [n_blocks, Hkv, block_size, dv]
  *   block_table int32 [B, max_blocks_per_seq]: logical key j of sequence b is
  *     slot j % block_size of physical block block_table[b, j / block_size];
  *   seq_lens int32 [B] on the device, each in [0, Sk_max]; sequence b has keys
@@ -150,7 +162,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  *   The caller guarantees table entries for j < seq_lens[b] are valid blocks.
  *
  * Gathered mode (row_index != NULL, block_table == NULL): Hkv must be 1 and Sq 1.
- *   k_cache, v_cache bf16 row arrays with a common row stride kv_row_stride
+ *   k_cache, v_cache row arrays with a common row stride kv_row_stride
  *     (elements, multiple of 8): the key of row r is k_cache[r*stride .. +dk),
  *     its value v_cache[r*stride .. +dv) (v_cache may alias k_cache, e.g. the
  *     value being the row's first dv columns).
@@ -159,7 +171,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  *   q_pos    int32 [B]: position of token b. With causal, key j is live iff
  *     key_pos[b, j] <= q_pos[b]; without causal every selected key is live.
  *   Sk_max must equal n_sel.
- *   k_cur, v_cur (optional, both or neither): bf16 rows [B, kv_row_stride]
+ *   k_cur, v_cur (optional, both or neither): rows [B, kv_row_stride] of kv_dtype
  *     holding token b's own key (first dk columns of k_cur row b) and value
  *     (first dv of v_cur row b); they join the selected rows as one more key at
  *     position q_pos[b], always live (the page's n_keys = n_prior + 1 with
@@ -171,7 +183,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  *   Two calls that share a workspace must be ordered on one stream.
  */
 attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
-                            void* o, int o_dtype,
+                            void* o, int o_dtype, int q_dtype, int kv_dtype,
                             int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv,
                             float scale, int causal, float softcap, const float* sinks,
                             const int32_t* block_table, int block_size, int max_blocks_per_seq,

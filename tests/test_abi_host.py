@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = binding.load_library()
     names = declared_functions()
-    assert {"attn_prefill_fwd", "attn_prefill_fwd_masked", "attn_decode_fwd",
+    assert {"attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_decode_fwd",
             "attn_decode_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), "symbol %s missing from libattn.so" % n
@@ -74,15 +74,15 @@ def test_prefill_rejects(kw, status):
     assert lib.attn_last_error().decode() != ""
 
 
-def prefill_masked(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, od=0, lse=None, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, dk=64, dv=64,
-             scale=0.125, causal=0, softcap=0.0, sinks=None, mask=FAKE, mb=1, mh=1, ms=8, max_bias=0.0,
+def prefill_ex(lib, **kw):
+    a = dict(q=FAKE, qd=0, k=FAKE, v=FAKE, kvd=0, o=FAKE, od=0, lse=None, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, dk=64,
+             dv=64, scale=0.125, causal=0, softcap=0.0, sinks=None, mask=FAKE, mb=1, mh=1, ms=8, max_bias=0.0,
              stream=None)
     a.update(kw)
-    return lib.attn_prefill_fwd_masked(a["q"], a["k"], a["v"], a["o"], a["od"], a["lse"], a["B"], a["Hq"],
-                                       a["Hkv"], a["Sq"], a["Sk"], a["dk"], a["dv"], a["scale"], a["causal"],
-                                       a["softcap"], a["sinks"], a["mask"], a["mb"], a["mh"], a["ms"],
-                                       a["max_bias"], a["stream"])
+    return lib.attn_prefill_fwd_ex(a["q"], a["qd"], a["k"], a["v"], a["kvd"], a["o"], a["od"], a["lse"], a["B"],
+                                   a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["dk"], a["dv"], a["scale"], a["causal"],
+                                   a["softcap"], a["sinks"], a["mask"], a["mb"], a["mh"], a["ms"], a["max_bias"],
+                                   a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -96,20 +96,23 @@ def prefill_masked(lib, **kw):
     (dict(max_bias=float("inf")), 1),
     (dict(Sq=1 << 20, Sk=1 << 20, ms=1 << 20), 2),     # one mask slab of 2 TiB
     (dict(dk=48, dv=48), 2),
+    (dict(qd=3), 1),                                   # unknown q dtype
+    (dict(kvd=1), 1),                                  # fp32 K/V are not an operand type
 ])
-def test_prefill_masked_rejects(kw, status):
+def test_prefill_ex_rejects(kw, status):
     lib = binding.load_library()
-    assert prefill_masked(lib, **kw) == status
+    assert prefill_ex(lib, **kw) == status
     assert lib.attn_last_error().decode() != ""
 
 
 def decode(lib, **kw):
-    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, od=0, B=2, Hq=8, Hkv=1, Sq=1, Sk_max=100, dk=128, dv=128,
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, o=FAKE, od=0, qd=0, kvd=0, B=2, Hq=8, Hkv=1, Sq=1, Sk_max=100, dk=128, dv=128,
              scale=0.1, causal=0, softcap=0.0, sinks=None, table=FAKE, bs=64, maxb=2, lens=FAKE,
              rows=None, kpos=None, qpos=None, n_sel=0, stride=0, kcur=None, vcur=None, ws=FAKE, ws_bytes=1 << 30,
              stream=None)
     a.update(kw)
-    return lib.attn_decode_fwd(a["q"], a["kc"], a["vc"], a["o"], a["od"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+    return lib.attn_decode_fwd(a["q"], a["kc"], a["vc"], a["o"], a["od"], a["qd"], a["kvd"], a["B"], a["Hq"],
+                               a["Hkv"], a["Sq"],
                                a["Sk_max"], a["dk"], a["dv"], a["scale"], a["causal"], a["softcap"], a["sinks"],
                                a["table"], a["bs"], a["maxb"], a["lens"], a["rows"], a["kpos"], a["qpos"],
                                a["n_sel"], a["stride"], a["kcur"], a["vcur"], a["ws"], a["ws_bytes"], a["stream"])
@@ -126,6 +129,8 @@ def decode(lib, **kw):
     (dict(ws=None), 1),
     (dict(Sq=1 << 12, Hq=512, Hkv=1), 2),                   # 2^21 query columns per KV head
     (dict(kcur=FAKE, vcur=FAKE), 1),                        # current rows in paged mode
+    (dict(qd=5), 1),                                        # unknown q dtype
+    (dict(kvd=1), 1),                                       # fp32 caches are not an operand type
     (dict(dk=100, dv=100), 2),
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, Hkv=2, Hq=8), 1),
     (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=128), 2),          # gathered (128,128)

@@ -1,4 +1,4 @@
-"""GPU parity of attn_prefill_fwd_masked (additive fp16 mask, ALiBi slopes) against the
+"""GPU parity of attn_prefill_fwd_ex with an additive fp16 mask and ALiBi slopes against the
 fp64 CPU oracle, through the C ABI."""
 
 import math
@@ -29,8 +29,8 @@ def check_masked(B, Sq, Sk, Hq, Hkv, dk, dv, MB, MH, kind="random", width=None, 
     o = torch.empty((B, Sq, Hq, dv), device="cuda", dtype=torch.float32 if o_dtype == "f32" else torch.bfloat16)
     lse = torch.empty((B, Hq, Sq), device="cuda", dtype=torch.float32)
     sk = dev(case["sinks"]) if case["sinks"] is not None else None
-    binding.attn_prefill_fwd_masked(q, k, v, o, dev(mask), lse, scale=scale, causal=causal, softcap=softcap,
-                                    sinks=sk, max_bias=max_bias)
+    binding.attn_prefill_fwd_ex(q, k, v, o, lse, scale=scale, causal=causal, softcap=softcap, sinks=sk,
+                                mask=dev(mask), max_bias=max_bias)
     torch.cuda.synchronize()
     ro, rl = oracle.prefill(case["q"], case["k"], case["v"], scale, causal=causal, softcap=softcap,
                             sinks=case["sinks"], mask=mask, max_bias=max_bias)
@@ -89,7 +89,7 @@ def test_zero_mask_matches_unmasked():
     o2 = torch.empty_like(o1)
     binding.attn_prefill_fwd(q, k, v, o1, scale=0.1, causal=True)
     mask = torch.zeros((1, 1, 256, 256), device="cuda", dtype=torch.float16)
-    binding.attn_prefill_fwd_masked(q, k, v, o2, mask, scale=0.1, causal=True)
+    binding.attn_prefill_fwd_ex(q, k, v, o2, scale=0.1, causal=True, mask=mask)
     torch.cuda.synchronize()
     ref, _ = oracle.prefill(case["q"], case["k"], case["v"], 0.1, causal=True)
     check_close(host(o1), ref, "f32", "unmasked")
