@@ -51,6 +51,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64",
+    "dequant_blocks",
     "alibi_slopes",
     "attend_rows",
     "prefill",
@@ -65,6 +66,31 @@ def bf16_bits_to_f64(bits):
     if b.dtype != np.uint16:
         raise TypeError("expected uint16 bf16 bit patterns, got %s" % b.dtype)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dequant_blocks(raw, fmt):
+    """Values of a block-quantized buffer (uint8 bytes), float64 [n_blocks * 32].
+
+    The "ggml-metal: FA tensor path" page has quantized K/V turned into fp16 by a
+    pre-pass before the fp16 kernels run; the block formats are off that page.
+    Reading taken (ggml's two plainest block formats, 32 values per block, an
+    IEEE fp16 scale d first, blocks packed back to back):
+      "q8_0": 34 bytes = d, then 32 int8 q;              value = d * q
+      "q4_0": 18 bytes = d, then 16 bytes of nibbles;     value = d * (q - 8),
+              byte j holds value j in its low nibble and value j + 16 in its high one.
+    """
+    raw = np.asarray(raw, dtype=np.uint8)
+    size = {"q8_0": 34, "q4_0": 18}[fmt]
+    if raw.size % size:
+        raise ValueError("buffer is not a whole number of blocks")
+    blk = raw.reshape(-1, size)
+    d = blk[:, :2].copy().view(np.float16).astype(np.float64)[:, 0]
+    if fmt == "q8_0":
+        q = blk[:, 2:].view(np.int8).astype(np.float64)
+    else:
+        nib = blk[:, 2:]
+        q = np.concatenate([nib & 0x0F, nib >> 4], axis=1).astype(np.float64) - 8.0
+    return (d[:, None] * q).reshape(-1)
 
 
 def _as_f64(a):

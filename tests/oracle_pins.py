@@ -356,6 +356,31 @@ def pin_gathered_current_row(orc):
     _close(o3, np.broadcast_to(cur[:, None, :5], o3.shape), 1e-15, "only the current row is live")
 
 
+def _block(d, payload):
+    return np.concatenate([np.frombuffer(np.float16(d).tobytes(), dtype=np.uint8),
+                           np.asarray(payload, dtype=np.uint8)])
+
+
+def pin_dequant_q8_0(orc):
+    """Hand-built q8_0 blocks: scale 0.5 with q = -16..15, then scale -2 with q = 127, -128, 0, ..."""
+    q1 = np.arange(-16, 16, dtype=np.int8)
+    q2 = np.zeros(32, dtype=np.int8)
+    q2[0], q2[1], q2[31] = 127, -128, 3
+    raw = np.concatenate([_block(0.5, q1.view(np.uint8)), _block(-2.0, q2.view(np.uint8))])
+    want = np.concatenate([0.5 * np.arange(-16, 16), np.zeros(32)])
+    want[32], want[33], want[63] = -254.0, 256.0, -6.0
+    _close(orc.dequant_blocks(raw, "q8_0"), want, 0.0, "q8_0 values")
+
+
+def pin_dequant_q4_0(orc):
+    """A q4_0 block with scale 0.25: byte j = (hi << 4) | lo gives values j (lo) and j + 16 (hi)."""
+    lo = np.arange(16, dtype=np.uint8)            # values 0..15   -> q - 8 = -8..7
+    hi = (15 - np.arange(16)).astype(np.uint8)    # values 16..31  -> 7..-8
+    raw = _block(0.25, (hi << 4) | lo)
+    want = 0.25 * np.concatenate([np.arange(16) - 8.0, 7.0 - np.arange(16)])
+    _close(orc.dequant_blocks(raw, "q4_0"), want, 0.0, "q4_0 values")
+
+
 # ---------------------------------------------------------------- additive mask, ALiBi
 def pin_alibi_slopes_published(orc):
     """The ALiBi slope schedule (Press, Smith and Lewis, "Train Short, Test Long"):

@@ -39,6 +39,9 @@ MUTATIONS = {
     "alibi_exponent_off_by_one": ("m0 ** (h + 1)", "m0 ** h"),
     "alibi_m1_base": ("m1 = 2.0 ** (-max_bias / 2.0 / n_log2)", "m1 = 2.0 ** (-max_bias / n_log2)"),
     "alibi_slope_ignored": ("bias = slopes[h] * mrows", "bias = mrows"),
+    "q4_0_nibble_order": ("q = np.concatenate([nib & 0x0F, nib >> 4], axis=1)", "q = np.stack([nib & 0x0F, nib >> 4], axis=2).reshape(len(nib), 32)"),
+    "q4_0_no_offset": (".astype(np.float64) - 8.0", ".astype(np.float64)"),
+    "q8_0_unsigned": ("q = blk[:, 2:].view(np.int8)", "q = blk[:, 2:].view(np.uint8)"),
     "current_row_masked": ("live_row = np.concatenate([live_row, [True]])",
                            "live_row = np.concatenate([live_row, [False]])"),
     "current_row_wrong_token": ("_as_f64(np.asarray(k_cur)[t])[None, :]", "_as_f64(np.asarray(k_cur)[0])[None, :]"),
