@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     attn_prefill_fwd_ex,
     attn_decode_fwd,
     attn_decode_workspace_bytes,
+    attn_dequant_fp16,
     attn_status_string,
     attn_abi_version,
     library_path,

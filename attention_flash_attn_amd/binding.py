@@ -22,6 +22,9 @@ ATTN_ERR_HIP = 3
 ATTN_BF16 = 0
 ATTN_F32 = 1
 ATTN_F16 = 2
+ATTN_Q8_0 = 0
+ATTN_Q4_0 = 1
+_QFMT = {"q8_0": (ATTN_Q8_0, 34), "q4_0": (ATTN_Q4_0, 18)}
 
 
 class AttnError(RuntimeError):
@@ -62,6 +65,8 @@ def load_library():
                                             c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                             c_float, c_int, c_float, c_void_p,
                                             c_void_p, c_int, c_int, ctypes.c_int64, c_float, c_void_p]
+        lib.attn_dequant_fp16.restype = c_int
+        lib.attn_dequant_fp16.argtypes = [c_void_p, c_int, c_void_p, ctypes.c_int64, c_void_p]
         lib.attn_decode_workspace_bytes.restype = c_size_t
         lib.attn_decode_workspace_bytes.argtypes = [c_int] * 7
         lib.attn_decode_fwd.restype = c_int
@@ -253,3 +258,17 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
                              _ptr(q_pos, "q_pos", torch.int32, True), n_sel, int(kv_row_stride),
                              kcp, vcp, _ptr(workspace, "workspace"), ws_bytes, _stream(stream))
     _check(st)
+
+
+def attn_dequant_fp16(src, fmt, dst, stream=None):
+    """src: uint8 GPU tensor of packed blocks ("q8_0": 34 bytes, "q4_0": 18 bytes per 32
+    values); dst: float16 GPU tensor with 32 elements per block. Enqueued on `stream`."""
+    import torch
+    lib = load_library()
+    code, size = _QFMT[fmt]
+    if src.dtype != torch.uint8 or src.numel() % size:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "src must be uint8 holding whole %s blocks" % fmt)
+    n = src.numel() // size
+    if dst.dtype != torch.float16 or dst.numel() != 32 * n:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "dst must be float16 with 32 elements per block")
+    _check(lib.attn_dequant_fp16(_ptr(src, "src"), code, _ptr(dst, "dst"), n, _stream(stream)))

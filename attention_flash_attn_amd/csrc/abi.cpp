@@ -243,4 +243,16 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
     return ok();
 }
 
+attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blocks, void* stream) {
+    if (fmt != ATTN_Q8_0 && fmt != ATTN_Q4_0) return fail(ATTN_ERR_INVALID_ARG, "fmt must be ATTN_Q8_0 or ATTN_Q4_0");
+    if (n_blocks < 0) return fail(ATTN_ERR_INVALID_ARG, "n_blocks must be >= 0");
+    if (n_blocks == 0) return ok();
+    if (!src || !dst) return fail(ATTN_ERR_INVALID_ARG, "src and dst are required");
+    if (!aligned16(src) || !aligned16(dst)) return fail(ATTN_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    if (n_blocks > ((int64_t)1 << 38)) return fail(ATTN_ERR_UNSUPPORTED, "too many blocks for one launch");
+    hipError_t e = attn::launch_dequant(src, fmt, dst, (long long)n_blocks, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "dequant launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

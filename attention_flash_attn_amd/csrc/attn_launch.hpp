@@ -73,4 +73,7 @@ bool decode_supported(int dk, int dv, bool gathered);
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
+// Block dequantization to fp16: fmt 0 = q8_0 (34-byte blocks), 1 = q4_0 (18-byte blocks).
+hipError_t launch_dequant(const void* src, int fmt, void* dst, long long n_blocks, hipStream_t stream);
+
 }  // namespace attn

@@ -194,6 +194,26 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
                             void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * Block formats of a quantized KV cache (32 values per block, IEEE fp16
+ * scale d first, blocks packed back to back with no padding).
+ */
+typedef enum attn_qfmt {
+    ATTN_Q8_0 = 0,   /* 34-byte blocks: d, 32 x int8 q; value = d * q */
+    ATTN_Q4_0 = 1    /* 18-byte blocks: d, 16 bytes; byte j holds q_j (low nibble) and
+                        q_{j+16} (high nibble); value = d * (q - 8) */
+} attn_qfmt;
+
+/*
+ * Dequantize n_blocks blocks of format fmt at src into IEEE fp16 dst
+ * [n_blocks * 32] (values in block order): the pre-pass the "ggml-metal: FA
+ * tensor path" page runs so that quantized K/V feed the fp16 kernels (then
+ * call the attention entry points with kv_dtype = ATTN_F16). d * q is exact in
+ * fp32 and rounded once to fp16 (nearest even). src and dst are device
+ * buffers, 16-byte aligned, not overlapping; n_blocks = 0 does nothing.
+ */
+attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -160,3 +160,15 @@ def test_workspace_bytes():
     assert n >= 16 * 128 * 8 * 514 * 4
     assert attn.attn_decode_workspace_bytes(0, 64, 8, 1, 100, 128, 128) == 0
     assert attn.attn_decode_workspace_bytes(2, 6, 4, 1, 100, 128, 128) == 0
+
+
+@pytest.mark.parametrize("fmt,src,dst,n,status", [
+    (2, FAKE, FAKE, 4, 1),                                   # unknown format
+    (0, FAKE, FAKE, -1, 1),
+    (0, None, FAKE, 4, 1),
+    (1, ctypes.c_void_p(0x10002), FAKE, 4, 1),                # misaligned source
+    (0, FAKE, FAKE, 0, 0),                                    # nothing to do (no launch)
+])
+def test_dequant_rejects(fmt, src, dst, n, status):
+    lib = binding.load_library()
+    assert lib.attn_dequant_fp16(src, fmt, dst, n, None) == status
