@@ -328,7 +328,7 @@ __device__ __forceinline__ void wait_stages(int later) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int DK, int DV, int NW, bool VK, bool F16>
+template <int DK, int DV, int NW, bool VK, bool F16, bool CAUSAL, bool SOFTCAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
 void decode_gathered_split_kernel(GatherParams p) {
     constexpr int NT = NW * 64;
@@ -343,9 +343,10 @@ void decode_gathered_split_kernel(GatherParams p) {
     constexpr int LPS = (NSEG / NW) * (VK ? 1 : 2);  // direct loads per wave per stage
     static_assert(DK % 32 == 0 && DV % 64 == 0 && DV <= DK && PITCH % 128 == 0 && PITCH % 256 != 0, "shape");
     static_assert(SSTAGE % 1024 == 0 && NSEG % NW == 0 && NCH % 8 == 0, "stage");
-    static_assert(NST * STAGE + 8 * kGatherMaxSplit <= 160 * 1024, "LDS");
+    static_assert(NST * STAGE + 12 * kGatherMaxSplit <= 160 * 1024, "LDS");
+    static_assert(NW * 16 * (DV + 4) * 4 <= NST * STAGE, "output staging fits the stages");
     __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
-    __shared__ int32_t srow[kGatherMaxSplit];
+    __shared__ long long skoff[kGatherMaxSplit];  // element offset of each key row from kc
     __shared__ __attribute__((aligned(16))) float spos[kGatherMaxSplit];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, c16 = lane & 15;
@@ -358,16 +359,37 @@ void decode_gathered_split_kernel(GatherParams p) {
     const int nk = nsel + has_cur;
     const float qpos = (float)p.q_pos[t];
 
-    for (int i = tid; i < nsel; i += NT) {
-        srow[i] = p.row_index[(size_t)t * p.n_sel + start + i];
-        spos[i] = p.key_pos[(size_t)t * p.n_sel + start + i];
+    // this split's row indices and positions (one per thread per pass)
+    constexpr int IPT = (kGatherMaxSplit + NT - 1) / NT;
+    long long roff_r[IPT];
+    float pos_r[IPT];
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+        const int i = tid + u * NT;
+        roff_r[u] = 0;
+        pos_r[u] = 0.f;
+        if (i < nsel) {
+            roff_r[u] = (long long)p.row_index[(size_t)t * p.n_sel + start + i];
+            pos_r[u] = p.key_pos[(size_t)t * p.n_sel + start + i];
+        }
+    }
+    // key rows as element offsets from kc (the token's own row from kcur), and positions
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+        const int i = tid + u * NT;
+        if (i < nsel) {
+            skoff[i] = roff_r[u] * p.row_stride;
+            spos[i] = pos_r[u];
+        }
     }
     if (has_cur && tid == 0) {
-        srow[nsel] = -1;  // rows come from kcur / vcur
+        skoff[nsel] = p.kcur_off + (long long)t * p.row_stride;
         spos[nsel] = qpos;
     }
     __syncthreads();
 
+    // query fragments (first needed by the first step's QK, so their latency hides
+    // under the first stages' copies)
     const int h = hgrp * (NW * 16) + wave * 16 + c16;
     const bool hok = h < p.Hq;
     bf16x8 qf[KQ];
@@ -382,22 +404,31 @@ void decode_gathered_split_kernel(GatherParams p) {
 
     // row r stores logical chunk c at chunk c ^ sw(r) (within aligned groups of 8)
     auto sw = [](int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); };
-    // Rows of step i into stage st: wave w fills 1 KB segments w, w+NW, ...
+    // Rows of step i into stage st: wave w fills 1 KB segments w, w+NW, ... All row offsets
+    // of the step are read from LDS before the first copy is issued (a copy writes LDS, so a
+    // later table read could not be moved ahead of it).
+    constexpr int JW = NSEG / NW;
     auto issue = [&](int i, int st) {
         char* sb = smem + st * STAGE;
+        long long ro[JW];
+        int kr[JW];
 #pragma unroll
-        for (int j = 0; j < NSEG / NW; ++j) {
+        for (int j = 0; j < JW; ++j) {
+            const int r = ((wave + j * NW) * 1024 + lane * 16) / PITCH;
+            kr[j] = min(i * 32 + r, nk - 1);
+            ro[j] = skoff[kr[j]];
+        }
+#pragma unroll
+        for (int j = 0; j < JW; ++j) {
             const int sg = wave + j * NW;
             const int off = sg * 1024 + lane * 16;
             const int r = off / PITCH;
             const int c = ((off - r * PITCH) >> 4) ^ sw(r);
-            const int kr = min(i * 32 + r, nk - 1);
-            const int row = srow[kr];
-            const long long rb = (long long)(row >= 0 ? row : t) * p.row_stride;
-            load_lds16(p.kc + (row >= 0 ? rb : p.kcur_off + rb) + c * 8, sb + sg * 1024);
+            load_lds16(p.kc + ro[j] + c * 8, sb + sg * 1024);
             if constexpr (!VK) {
                 // value rows use the same layout; chunks past the value width repeat earlier ones
-                load_lds16(p.vc + (row >= 0 ? rb : p.vcur_off + rb) + (c % (DV / 8)) * 8, sb + SSTAGE + sg * 1024);
+                const long long vo = ro[j] + ((has_cur && kr[j] == nsel) ? p.vcur_off - p.kcur_off : 0);
+                load_lds16(p.vc + vo + (c % (DV / 8)) * 8, sb + SSTAGE + sg * 1024);
             }
         }
     };
@@ -430,7 +461,7 @@ void decode_gathered_split_kernel(GatherParams p) {
         const char* vt = VK ? kt : kt + SSTAGE;
         const int r0 = i * 32;
         f32x4 kpos[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        if (p.causal) {
+        if constexpr (CAUSAL) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) kpos[kb] = *(const f32x4*)(spos + r0 + kb * 16 + grp * 4);
         }
@@ -464,14 +495,14 @@ void decode_gathered_split_kernel(GatherParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float x = sc[kb][e];
-                if (p.softcap_on) {
+                if constexpr (SOFTCAP) {
                     const float ex = exp2_fast(x * p.c_tanh);
                     x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(ex + 1.f);
                 } else {
                     x *= p.c_score;
                 }
-                const int kl = r0 + kb * 16 + grp * 4 + e;
-                const bool live = kl < nk && (!p.causal || kpos[kb][e] <= qpos);
+                const int kl = r0 + kb * 16 + grp * 4 + e;  // key within the split
+                const bool live = kl < nk && (!CAUSAL || kpos[kb][e] <= qpos);
                 if (!live) x = -INFINITY;
                 sc[kb][e] = x;
                 mx = fmaxf(mx, x);
@@ -517,16 +548,28 @@ void decode_gathered_split_kernel(GatherParams p) {
     }
 
     const float l_tot = quarterwave_sum(l_run);
-    if (hok) {
-        const size_t row = (size_t)t * p.Hq + h;
-        const size_t slot = row * p.n_split + split;
-        if (grp == 0) {
-            p.ws_ml[slot * 2] = m_run;
-            p.ws_ml[slot * 2 + 1] = l_tot;
-        }
-        float* op = p.ws_o + slot * DV;
+    if (hok && grp == 0) {
+        const size_t slot = ((size_t)t * p.Hq + h) * p.n_split + split;
+        p.ws_ml[slot * 2] = m_run;
+        p.ws_ml[slot * 2 + 1] = l_tot;
+    }
+    // Partial O through LDS (the stages are free once every wave is past its last step), so
+    // each store instruction writes 1 KB of contiguous partial row: the wave's 16 heads at a
+    // row pitch of DV + 4 floats (conflict-free writes of the O^T fragments).
+    constexpr int OP = DV + 4;
+    __syncthreads();
+    float* ost = (float*)smem + wave * 16 * OP;
 #pragma unroll
-        for (int d = 0; d < DBV; ++d) *(f32x4*)(op + d * 16 + grp * 4) = oacc[d];
+    for (int d = 0; d < DBV; ++d) *(f32x4*)(ost + c16 * OP + d * 16 + grp * 4) = oacc[d];
+    // (a wave's LDS accesses complete in order, so it reads its own writes back directly)
+#pragma unroll 4
+    for (int k = 0; k < 16 * DV / 256; ++k) {  // 256 floats per instruction
+        const int hh = (k * 256) / DV, col = (k * 256) % DV + lane * 4;
+        const int head = hgrp * (NW * 16) + wave * 16 + hh;
+        if (head < p.Hq) {
+            const size_t slot = ((size_t)t * p.Hq + head) * p.n_split + split;
+            *(f32x4*)(p.ws_o + slot * DV + col) = *(const f32x4*)(ost + hh * OP + col);
+        }
     }
 }
 
@@ -633,6 +676,30 @@ hipError_t launch_paged_t(const SplitParams& sp, dim3 grid, hipStream_t stream) 
 template <int DK, int DV>
 hipError_t launch_paged(const SplitParams& sp, bool f16, dim3 grid, hipStream_t stream) {
     return f16 ? launch_paged_t<DK, DV, true>(sp, grid, stream) : launch_paged_t<DK, DV, false>(sp, grid, stream);
+}
+
+template <int NW, bool VK, bool F16, bool CAUSAL, bool SOFTCAP>
+hipError_t launch_gathered_t(const GatherParams& gp, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, VK, F16, CAUSAL, SOFTCAP>), grid, dim3(NW * 64), 0,
+                       stream, gp);
+    return hipGetLastError();
+}
+template <int NW, bool VK, bool F16>
+hipError_t launch_gathered_f(const GatherParams& gp, bool causal, bool softcap, dim3 grid, hipStream_t stream) {
+    if (causal)
+        return softcap ? launch_gathered_t<NW, VK, F16, true, true>(gp, grid, stream)
+                       : launch_gathered_t<NW, VK, F16, true, false>(gp, grid, stream);
+    return softcap ? launch_gathered_t<NW, VK, F16, false, true>(gp, grid, stream)
+                   : launch_gathered_t<NW, VK, F16, false, false>(gp, grid, stream);
+}
+template <int NW>
+hipError_t launch_gathered(const GatherParams& gp, bool vk, bool f16, bool causal, bool softcap, dim3 grid,
+                           hipStream_t stream) {
+    if (vk)
+        return f16 ? launch_gathered_f<NW, true, true>(gp, causal, softcap, grid, stream)
+                   : launch_gathered_f<NW, true, false>(gp, causal, softcap, grid, stream);
+    return f16 ? launch_gathered_f<NW, false, true>(gp, causal, softcap, grid, stream)
+               : launch_gathered_f<NW, false, false>(gp, causal, softcap, grid, stream);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, const DecodePlan& pl, float* ws_o, float* ws_ml,
@@ -755,22 +822,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         constexpr int NW = 4;
         const dim3 ggrid((unsigned)pl.n_split, (unsigned)((a.Hq + NW * 16 - 1) / (NW * 16)), (unsigned)a.B);
         const bool vk = a.v_cache == a.k_cache;
-        if (a.kv_f16) {
-            if (vk)
-                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, true, true>), ggrid, dim3(NW * 64), 0,
-                                   stream, gp);
-            else
-                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, false, true>), ggrid, dim3(NW * 64), 0,
-                                   stream, gp);
-        } else {
-            if (vk)
-                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, true, false>), ggrid, dim3(NW * 64), 0,
-                                   stream, gp);
-            else
-                hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, false, false>), ggrid, dim3(NW * 64), 0,
-                                   stream, gp);
-        }
-        e = hipGetLastError();
+        e = launch_gathered<NW>(gp, vk, a.kv_f16 != 0, a.causal != 0, sp.softcap_on != 0, ggrid, stream);
         if (e != hipSuccess) return e;
         return launch_combine(a, pl, ws_o, ws_ml, nullptr, stream);
     }
