@@ -203,7 +203,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "prefill_kernel<128,128,64,bf16 out>",
+            "kernel": "prefill_kernel<128,128,64,8,2,causal,bf16 out>",
             "bound": "mfma",
             "achieved": round(tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -306,6 +306,61 @@ def main():
             log("%s: %.1f us, %.1f TFLOP/s" % (name, t * 1e6, f / t / 1e12))
             del q, k, v, o, cc
         result["other"] = other
+
+        # the widened operations at the same workload shapes (own timing)
+        def timed(fn, reps=10):
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.025:  # at least 25 ms of warm work: steady clocks
+                fn()
+                torch.cuda.synchronize()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            z.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(z) * 1e-3 / reps
+
+        variants = {}
+        log("variants: ALiBi mask, fp16 K/V, multi-token decode, q8_0 pre-pass")
+        mask2 = torch.from_numpy(synth.mask_case(2, 1, 1, c2["Sq"], c2["Sk"], kind="distance")).to(dev)
+        t = timed(lambda: binding.attn_prefill_fwd_ex(q2, k2, v2, o2, scale=c2["scale"], causal=True, mask=mask2,
+                                                      max_bias=8.0))
+        variants["prefill_c2_alibi"] = {"workload": "config 2 + fp16 distance mask [1,1,4096,4096], max_bias 8",
+                                        "us": round(t * 1e6, 1), "TFLOP/s": round(flops2 / t / 1e12, 1)}
+        del mask2
+        q2f, k2h, v2h = q2.float(), k2.half(), v2.half()
+        t = timed(lambda: binding.attn_prefill_fwd_ex(q2f, k2h, v2h, o2, scale=c2["scale"], causal=True))
+        variants["prefill_c2_f16kv_f32q"] = {"workload": "config 2 with fp16 K/V and an fp32 Q",
+                                             "us": round(t * 1e6, 1), "TFLOP/s": round(flops2 / t / 1e12, 1)}
+        del q2f, k2h, v2h
+        kc4h, vc4h = kc4.half(), vc4.half()
+        t = timed(lambda: binding.attn_decode_fwd(q4, kc4h, vc4h, o4, ws4, scale=c4["scale"], Sk_max=c4["len_hi"],
+                                                  block_table=table4, seq_lens=lens4))
+        variants["decode_c4_f16"] = {"workload": "config 4 with fp16 caches", "us": round(t * 1e6, 1),
+                                     "GB/s": round(bytes4 / t / 1e9, 1)}
+        del kc4h, vc4h
+        q4s = torch.randn((c4["B"], 4, c4["Hq"], c4["dk"]), device=dev).to(torch.bfloat16)
+        o4s = torch.empty((c4["B"], 4, c4["Hq"], c4["dv"]), device=dev, dtype=torch.bfloat16)
+        ws4s = torch.empty(binding.attn_decode_workspace_bytes(c4["B"], c4["Hq"], c4["Hkv"], 4, c4["len_hi"],
+                                                               c4["dk"], c4["dv"]), device=dev, dtype=torch.uint8)
+        t = timed(lambda: binding.attn_decode_fwd(q4s, kc4, vc4, o4s, ws4s, scale=c4["scale"], Sk_max=c4["len_hi"],
+                                                  causal=True, block_table=table4, seq_lens=lens4))
+        variants["decode_c4_4tokens"] = {"workload": "config 4 with 4 causal draft tokens per sequence "
+                                                     "(32 query columns per KV head)",
+                                         "us": round(t * 1e6, 1), "GB/s": round(bytes4 / t / 1e9, 1)}
+        del q4s, o4s, ws4s
+        nblk = 1 << 24
+        src = torch.randint(0, 256, (nblk * 34,), device=dev, dtype=torch.uint8)
+        dst = torch.empty(nblk * 32, device=dev, dtype=torch.float16)
+        t = timed(lambda: binding.attn_dequant_fp16(src, "q8_0", dst))
+        variants["dequant_q8_0"] = {"workload": "2^24 q8_0 blocks (571 MB) to fp16 (1074 MB)",
+                                    "us": round(t * 1e6, 1),
+                                    "GB/s": round((src.numel() + dst.numel() * 2) / t / 1e9, 1)}
+        del src, dst
+        for k, v in variants.items():
+            log("%s: %s" % (k, ", ".join("%s %s" % (a, b) for a, b in v.items() if a != "workload")))
+        result["variants"] = variants
 
     # ---------------- CPU baseline: the oracle on a bounded sample of the prefill workload
     if not args.no_cpu:
