@@ -20,6 +20,10 @@ and all index structure come from one PCG64(seed) stream in the order below.
     permuted blocks of 64 rows, q, then per token a position q_pos ~
     U{n_sel-1..n_rows-1} and n_sel distinct positions <= q_pos (sorted);
     row_index is the physical row of each position, key_pos its fp32 value.
+  * MLA tail: the latent attention output o_lat [T, H, R] ~ N(0, 1) (tag 0),
+    out-absorb weights [H, DV, R] ~ N(0, 1/R) (tag 1) and o-projection weights
+    [H*DV, N] ~ N(0, 1/(H*DV)) (tag 2), so u and y stay of order 1 (random
+    weights of the model's shapes; no trained values).
 """
 
 import os
@@ -34,7 +38,9 @@ __all__ = [
     "prefill_case",
     "paged_case",
     "gathered_case",
+    "mla_tail_case",
     "CONFIGS",
+    "MLA_TAIL",
 ]
 
 
@@ -200,6 +206,13 @@ def gathered_case(seed, T, Hq, dk, dv, n_rows, n_sel, row_dim=None, block_rows=6
             "sinks": s}
 
 
+def mla_tail_case(seed, T, H, R, DV, N):
+    """MLA tail inputs: o_lat [T,H,R], w_absorb [H,DV,R], w_o [H*DV,N], all bf16 bits."""
+    return {"o_lat": normal_bf16(seed, 0, (T, H, R)),
+            "w_absorb": normal_bf16(seed, 1, (H, DV, R), std=R ** -0.5),
+            "w_o": normal_bf16(seed, 2, (H * DV, N), std=(H * DV) ** -0.5)}
+
+
 # The five workloads the path is measured and checked on. Each entry says what
 # its inputs are; seeds 1..5.
 CONFIGS = {
@@ -219,3 +232,8 @@ CONFIGS = {
                                    n_sel=2048, row_dim=576, scale=1.0 / 24, causal=True, softcap=0.0,
                                    sinks=False, o_dtype="bf16"),
 }
+
+# The tail that follows the gathered MLA decode: its 16 tokens x 128 heads of
+# 512-wide latent output, v_head_dim 128 and hidden width 7168 (DeepSeek-V3's
+# published model shape; the page names the model but not the widths), seed 6.
+MLA_TAIL = dict(seed=6, T=16, H=128, R=512, DV=128, N=7168)

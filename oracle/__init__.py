@@ -5,4 +5,4 @@ import this package; the HIP path never does, and this package never imports
 the HIP path.
 """
 
-from .oracle import bf16_bits_to_f64, dequant_blocks, alibi_slopes, attend_rows, prefill, decode_paged, decode_gathered  # noqa: F401
+from .oracle import bf16_bits_to_f64, dequant_blocks, alibi_slopes, attend_rows, prefill, decode_paged, decode_gathered, mla_tail  # noqa: F401

@@ -57,6 +57,7 @@ __all__ = [
     "prefill",
     "decode_paged",
     "decode_gathered",
+    "mla_tail",
 ]
 
 
@@ -295,3 +296,32 @@ def decode_gathered(q, k_rows, v_rows, row_index, key_pos, q_pos, scale,
             o[ti, h, :] = ob[0]
             lse[ti, h] = lb[0]
     return o, lse
+
+
+def mla_tail(o_lat, w_absorb, w_o):
+    """The two projections after MLA decode attention, per token.
+
+    "MLA Decode Attention Kernel API Reference" page, Background and the
+    out_absorb_w / o_proj_w parameters: the attention output of head h lives in
+    the cache's latent space (width R = kv_lora_rank); the head's slice of the
+    out-absorb weight [DV, R] maps it to v_head_dim values, and the o-projection
+    [H * DV, N] maps the heads' values, head after head, to the hidden width:
+
+        u[t, h, v] = sum_c w_absorb[h, v, c] * o_lat[t, h, c]
+        y[t, n]    = sum_h sum_v u[t, h, v] * w_o[h * DV + v, n]
+
+    o_lat [T, H, R], w_absorb [H, DV, R], w_o [H * DV, N] (bf16 bit patterns or
+    floats). Returns (y [T, N], u [T, H, DV]) in float64, nothing rounded.
+    """
+    o = _as_f64(o_lat)
+    wa = _as_f64(w_absorb)
+    wo = _as_f64(w_o)
+    T, H, R = o.shape
+    DV = wa.shape[1]
+    if wa.shape != (H, DV, R) or wo.shape[0] != H * DV:
+        raise ValueError("shape mismatch: o_lat %s, w_absorb %s, w_o %s" % (o.shape, wa.shape, wo.shape))
+    u = np.empty((T, H, DV))
+    for h in range(H):
+        u[:, h, :] = o[:, h, :] @ wa[h].T
+    y = u.reshape(T, H * DV) @ wo
+    return y, u

@@ -477,4 +477,52 @@ def pin_mask_all_neg_inf(orc):
     assert np.isfinite(lse[0, 0, [0, 2]]).all()
 
 
+
+# ---------------------------------------------------------------- MLA tail (out-absorb, o-projection)
+def pin_mla_tail_hand_example(orc):
+    """One token, two heads, latent width 3, v_head_dim 2, hidden 2, worked by hand
+    ("MLA Decode Attention Kernel API Reference" page, out_absorb_w [n_heads,
+    v_head_dim, kv_lora_rank] and o_proj_w [n_heads * v_head_dim, hidden]):
+        head 0: o = (1, 2, 0),  W = [[1, 0, 1], [0, 1, 0]]   -> u = (1, 2)
+        head 1: o = (0, 1, -1), W = [[0, 3, 0], [1, 0, -1]]  -> u = (3, 1)
+        rows of w_o, head-major: (1, 0), (0, 1), (1, 1), (2, -1)
+        y = 1*(1, 0) + 2*(0, 1) + 3*(1, 1) + 1*(2, -1) = (6, 4)"""
+    o_lat = np.array([[[1.0, 2.0, 0.0], [0.0, 1.0, -1.0]]])
+    w_abs = np.array([[[1.0, 0.0, 1.0], [0.0, 1.0, 0.0]], [[0.0, 3.0, 0.0], [1.0, 0.0, -1.0]]])
+    w_o = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [2.0, -1.0]])
+    y, u = orc.mla_tail(o_lat, w_abs, w_o)
+    _close(u, [[[1.0, 2.0], [3.0, 1.0]]], 0.0, "hand example u")
+    _close(y, [[6.0, 4.0]], 0.0, "hand example y")
+
+
+def pin_mla_tail_identity_absorb(orc):
+    """With v_head_dim equal to the latent width and every head's out-absorb the
+    identity, u is the attention output itself and the tail is one plain matrix
+    product of the tokens' concatenated heads with w_o (numpy's matmul)."""
+    rng = _rng(70)
+    T, H, R, N = 3, 4, 8, 5
+    o_lat = _rand(rng, T, H, R)
+    w_abs = np.broadcast_to(np.eye(R), (H, R, R)).copy()
+    w_o = _rand(rng, H * R, N)
+    y, u = orc.mla_tail(o_lat, w_abs, w_o)
+    _close(u, o_lat, 0.0, "identity absorb gives u = o")
+    _close(y, np.matmul(o_lat.reshape(T, H * R), w_o), 1e-12, "identity absorb gives one matmul")
+
+
+def pin_mla_tail_head_rescale(orc):
+    """Scaling head h's out-absorb by s_h and its rows of w_o by 1 / s_h leaves y
+    unchanged and scales u[:, h] by s_h: each head's value block meets its own
+    o-projection rows (bilinearity of the two products)."""
+    rng = _rng(71)
+    T, H, R, DV, N = 2, 3, 6, 4, 7
+    o_lat = _rand(rng, T, H, R)
+    w_abs = _rand(rng, H, DV, R)
+    w_o = _rand(rng, H * DV, N)
+    s = np.array([2.0, -0.5, 4.0])
+    y1, u1 = orc.mla_tail(o_lat, w_abs, w_o)
+    y2, u2 = orc.mla_tail(o_lat, w_abs * s[:, None, None], w_o / np.repeat(s, DV)[:, None])
+    _close(y1, y2, 1e-12, "y under per-head rescaling")
+    _close(u2, u1 * s[None, :, None], 1e-12, "u scales with its head")
+
+
 PINS = {name[4:]: fn for name, fn in sorted(globals().items()) if name.startswith("pin_") and callable(fn)}

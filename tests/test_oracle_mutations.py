@@ -45,6 +45,9 @@ MUTATIONS = {
     "current_row_masked": ("live_row = np.concatenate([live_row, [True]])",
                            "live_row = np.concatenate([live_row, [False]])"),
     "current_row_wrong_token": ("_as_f64(np.asarray(k_cur)[t])[None, :]", "_as_f64(np.asarray(k_cur)[0])[None, :]"),
+    "tail_absorb_layout_r_major": ("u[:, h, :] = o[:, h, :] @ wa[h].T", "u[:, h, :] = o[:, h, :] @ wa[h].reshape(R, DV)"),
+    "tail_absorb_wrong_head": ("u[:, h, :] = o[:, h, :] @ wa[h].T", "u[:, h, :] = o[:, h, :] @ wa[(h + 1) % H].T"),
+    "tail_concat_value_major": ("y = u.reshape(T, H * DV) @ wo", "y = u.transpose(0, 2, 1).reshape(T, H * DV) @ wo"),
 }
 
 
