@@ -1,4 +1,4 @@
-"""MI355X-native fused scaled-dot-product attention (prefill + paged / gathered decode).
+"""MI355X-native fused scaled-dot-product attention (prefill, paged / gathered decode, MLA decode tail).
 
 The compute path is the C-ABI library libattn.so (hand-written HIP kernels for
 gfx950); this package is its thin Python binding. Importing the package does
@@ -13,6 +13,8 @@ from .binding import (  # noqa: F401
     attn_decode_fwd,
     attn_decode_workspace_bytes,
     attn_dequant_fp16,
+    attn_mla_tail,
+    attn_mla_tail_workspace_bytes,
     attn_status_string,
     attn_abi_version,
     library_path,

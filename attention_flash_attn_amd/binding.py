@@ -76,6 +76,11 @@ def load_library():
                                         c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_int, ctypes.c_int64,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        lib.attn_mla_tail_workspace_bytes.restype = c_size_t
+        lib.attn_mla_tail_workspace_bytes.argtypes = [c_int] * 5
+        lib.attn_mla_tail.restype = c_int
+        lib.attn_mla_tail.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                      c_int, c_int, c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]
         _LIB = lib
         return lib
 
@@ -272,3 +277,28 @@ def attn_dequant_fp16(src, fmt, dst, stream=None):
     if dst.dtype != torch.float16 or dst.numel() != 32 * n:
         raise AttnError(ATTN_ERR_INVALID_ARG, "dst must be float16 with 32 elements per block")
     _check(lib.attn_dequant_fp16(_ptr(src, "src"), code, _ptr(dst, "dst"), n, _stream(stream)))
+
+
+def attn_mla_tail_workspace_bytes(T, H, R, DV, N):
+    return int(load_library().attn_mla_tail_workspace_bytes(T, H, R, DV, N))
+
+
+def attn_mla_tail(o_lat, w_absorb, w_o, y, workspace, stream=None):
+    """MLA decode tail. o_lat bf16 [T, H, R] (or [T, 1, H, R]), w_absorb bf16 [H, DV, R],
+    w_o bf16 [H*DV, N], y [T, N] bf16 or float32, workspace a uint8 GPU tensor of at least
+    attn_mla_tail_workspace_bytes(T, H, R, DV, N) bytes. Enqueued on `stream`."""
+    import torch
+    lib = load_library()
+    if w_absorb.dim() != 3 or w_o.dim() != 2 or y.dim() != 2:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "w_absorb must be [H, DV, R], w_o [H*DV, N] and y [T, N]")
+    H, DV, R = w_absorb.shape
+    N = w_o.shape[1]
+    T = y.shape[0]
+    if o_lat.numel() != T * H * R or w_o.shape[0] != H * DV or y.shape[1] != N:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "shape mismatch: o_lat %s, w_absorb %s, w_o %s, y %s" %
+                        (tuple(o_lat.shape), tuple(w_absorb.shape), tuple(w_o.shape), tuple(y.shape)))
+    ycode = _odtype(y)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.attn_mla_tail(_ptr(o_lat, "o_lat", torch.bfloat16), _ptr(w_absorb, "w_absorb", torch.bfloat16),
+                             _ptr(w_o, "w_o", torch.bfloat16), _ptr(y, "y"), ycode, T, H, R, DV, N,
+                             _ptr(workspace, "workspace"), ws_bytes, _stream(stream)))

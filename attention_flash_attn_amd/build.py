@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libattn.so")
-SOURCES = ["prefill.hip", "decode.hip", "dequant.hip", "abi.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "dequant.hip", "mla_tail.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 

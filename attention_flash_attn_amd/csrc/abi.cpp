@@ -255,4 +255,48 @@ attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blo
     return ok();
 }
 
+size_t attn_mla_tail_workspace_bytes(int T, int H, int R, int DV, int N) {
+    if (T <= 0 || H <= 0 || R <= 0 || DV <= 0 || N <= 0) return 0;
+    return attn::tail_plan(T, H, R, DV, N).ws_bytes;
+}
+
+attn_status attn_mla_tail(const void* o_lat, const void* w_absorb, const void* w_o, void* y, int y_dtype, int T,
+                          int H, int R, int DV, int N, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!o_lat || !w_absorb || !w_o || !y || !workspace)
+        return fail(ATTN_ERR_INVALID_ARG, "o_lat, w_absorb, w_o, y and workspace are required");
+    if (T <= 0 || H <= 0 || R <= 0 || DV <= 0 || N <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (T=%d H=%d R=%d DV=%d N=%d)", T, H, R, DV, N);
+    if (y_dtype != ATTN_BF16 && y_dtype != ATTN_F32)
+        return fail(ATTN_ERR_INVALID_ARG, "y_dtype must be ATTN_BF16 or ATTN_F32");
+    if (R % 128 != 0) return fail(ATTN_ERR_INVALID_ARG, "R (%d) must be a multiple of 128", R);
+    if (DV % 16 != 0) return fail(ATTN_ERR_INVALID_ARG, "DV (%d) must be a multiple of 16", DV);
+    const long long K = (long long)H * DV;
+    if (K % 128 != 0) return fail(ATTN_ERR_INVALID_ARG, "H * DV (%lld) must be a multiple of 128", K);
+    if (N % 128 != 0) return fail(ATTN_ERR_INVALID_ARG, "N (%d) must be a multiple of 128", N);
+    if (N / 128 > 65535) return fail(ATTN_ERR_INVALID_ARG, "N (%d) exceeds 128 * 65535", N);
+    if (K > INT32_MAX / 2 || (long long)H * (DV / 16) > INT32_MAX)
+        return fail(ATTN_ERR_INVALID_ARG, "H * DV (%lld) too large", K);
+    if (!aligned16(o_lat) || !aligned16(w_absorb) || !aligned16(w_o) || !aligned16(y) || !aligned16(workspace))
+        return fail(ATTN_ERR_INVALID_ARG, "o_lat, w_absorb, w_o, y and workspace must be 16-byte aligned");
+    const attn::TailPlan pl = attn::tail_plan(T, H, R, DV, N);
+    if (workspace_bytes < pl.ws_bytes)
+        return fail(ATTN_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes,
+                    pl.ws_bytes);
+    attn::TailArgs a;
+    a.o_lat = o_lat;
+    a.w_absorb = w_absorb;
+    a.w_o = w_o;
+    a.y = y;
+    a.y_f32 = y_dtype == ATTN_F32;
+    a.T = T;
+    a.H = H;
+    a.R = R;
+    a.DV = DV;
+    a.N = N;
+    a.workspace = workspace;
+    hipError_t e = attn::launch_mla_tail(a, pl, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "MLA tail launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -76,4 +76,25 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
 // Block dequantization to fp16: fmt 0 = q8_0 (34-byte blocks), 1 = q4_0 (18-byte blocks).
 hipError_t launch_dequant(const void* src, int fmt, void* dst, long long n_blocks, hipStream_t stream);
 
+// MLA decode tail: u = bf16(per-head out-absorb of o_lat), y = u @ w_o (split-K, fp32 partials).
+struct TailArgs {
+    const void* o_lat;     // bf16 [T, H, R]
+    const void* w_absorb;  // bf16 [H, DV, R]
+    const void* w_o;       // bf16 [H * DV, N]
+    void* y;               // [T, N], bf16 or fp32
+    int y_f32;
+    int T, H, R, DV, N;
+    void* workspace;
+};
+
+struct TailPlan {
+    int ks;           // K slices of the o-projection grid
+    int kslice;       // K rows per slice (a multiple of 128)
+    size_t u_bytes;   // bf16 u [T, H * DV], rounded up to 256 bytes
+    size_t ws_bytes;  // u + fp32 partials [ks, T, N]
+};
+
+TailPlan tail_plan(int T, int H, int R, int DV, int N);
+hipError_t launch_mla_tail(const TailArgs& a, const TailPlan& plan, hipStream_t stream);
+
 }  // namespace attn

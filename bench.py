@@ -358,6 +358,28 @@ def main():
                                     "us": round(t * 1e6, 1),
                                     "GB/s": round((src.numel() + dst.numel() * 2) / t / 1e9, 1)}
         del src, dst
+        # MLA decode tail after config 5: out-absorb + o-projection for its 16 tokens x 128 heads;
+        # two weight copies alternate so the 252 MB of weights come from HBM each call
+        tc = synth.MLA_TAIL
+        T_, H_, R_, DV_, N_ = tc["T"], tc["H"], tc["R"], tc["DV"], tc["N"]
+        ol = torch.randn((T_, H_, R_), device=dev).to(torch.bfloat16)
+        was = [(torch.randn((H_, DV_, R_), device=dev) * R_ ** -0.5).to(torch.bfloat16) for _ in range(2)]
+        wos = [(torch.randn((H_ * DV_, N_), device=dev) * (H_ * DV_) ** -0.5).to(torch.bfloat16) for _ in range(2)]
+        yt = torch.empty((T_, N_), device=dev, dtype=torch.bfloat16)
+        wst = torch.empty(binding.attn_mla_tail_workspace_bytes(T_, H_, R_, DV_, N_), device=dev, dtype=torch.uint8)
+        it = [0]
+
+        def tail_call():
+            i = it[0] = (it[0] + 1) % 2
+            binding.attn_mla_tail(ol, was[i], wos[i], yt, wst)
+        t = timed(tail_call, reps=20)
+        tail_bytes = (H_ * DV_ * R_ + H_ * DV_ * N_ + T_ * H_ * R_ + T_ * N_) * 2
+        tail_flops = 2.0 * T_ * H_ * DV_ * (R_ + N_)
+        variants["mla_tail"] = {"workload": "MLA tail after config 5: 16 tokens, 128 heads, latent 512, "
+                                            "v_head_dim 128, hidden 7168 (252 MB of bf16 weights, cold)",
+                                "us": round(t * 1e6, 1), "GB/s": round(tail_bytes / t / 1e9, 1),
+                                "TFLOP/s": round(tail_flops / t / 1e12, 2)}
+        del ol, was, wos, yt, wst
         for k, v in variants.items():
             log("%s: %s" % (k, ", ".join("%s %s" % (a, b) for a, b in v.items() if a != "workload")))
         result["variants"] = variants

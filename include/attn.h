@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum attn_status {
     ATTN_OK = 0,
@@ -213,6 +213,34 @@ typedef enum attn_qfmt {
  * buffers, 16-byte aligned, not overlapping; n_blocks = 0 does nothing.
  */
 attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blocks, void* stream);
+
+/*
+ * MLA decode tail: the out-absorb and the o-projection that follow MLA decode
+ * attention ("MLA Decode Attention Kernel API Reference" page: Background, the
+ * out_absorb_w and o_proj_w parameters, Notes: both are batched across the
+ * tokens). With K = H * DV:
+ *   u[t, h*DV + v] = sum_c w_absorb[h, v, c] * o_lat[t, h, c]   (fp32, rounded to bf16)
+ *   y[t, n]        = sum_k u[t, k] * w_o[k, n]                   (fp32 accumulation)
+ *   o_lat     bf16 [T, H, R]   the latent attention output (attn_decode_fwd's
+ *                              gathered-mode o with dv = R and o_dtype ATTN_BF16)
+ *   w_absorb  bf16 [H, DV, R]  each head's value half of the KV up-projection
+ *   w_o       bf16 [K, N]      the o-projection, rows head-major (row h*DV + v)
+ *   y         [T, N] contiguous, element type y_dtype (ATTN_BF16 or ATTN_F32);
+ *             bf16 results are rounded to nearest even from the fp32 sum.
+ * Requirements: T, H >= 1; R a multiple of 128; DV a multiple of 16; K a
+ * multiple of 128; N a multiple of 128 (at most 128 * 65535); every pointer
+ * 16-byte aligned; workspace (device, caller-owned, at least
+ * attn_mla_tail_workspace_bytes(T, H, R, DV, N) bytes, 16-byte aligned) holds u
+ * and the fp32 partial sums of the K slices; it is fully overwritten. The
+ * K slices are added in a fixed order, so results are run-to-run identical.
+ * All buffers are device memory and must not overlap. Errors:
+ * ATTN_ERR_INVALID_ARG for NULL or misaligned pointers, sizes that break the
+ * rules above, or a workspace that is too small; nothing is launched then.
+ */
+size_t attn_mla_tail_workspace_bytes(int T, int H, int R, int DV, int N);
+attn_status attn_mla_tail(const void* o_lat, const void* w_absorb, const void* w_o, void* y, int y_dtype,
+                          int T, int H, int R, int DV, int N,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

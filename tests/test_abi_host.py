@@ -172,3 +172,36 @@ def test_workspace_bytes():
 def test_dequant_rejects(fmt, src, dst, n, status):
     lib = binding.load_library()
     assert lib.attn_dequant_fp16(src, fmt, dst, n, None) == status
+
+
+def tail(lib, **kw):
+    a = dict(o=FAKE, wa=FAKE, wo=FAKE, y=FAKE, yd=0, T=16, H=8, R=128, DV=32, N=256, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.attn_mla_tail(a["o"], a["wa"], a["wo"], a["y"], a["yd"], a["T"], a["H"], a["R"], a["DV"], a["N"],
+                             a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1),
+    (dict(ws=None), 1),
+    (dict(T=0), 1),
+    (dict(yd=2), 1),                          # fp16 output is not offered
+    (dict(R=96), 1),                          # latent width not a multiple of 128
+    (dict(DV=24), 1),                         # v_head_dim not a multiple of 16
+    (dict(H=3, DV=16), 1),                    # H * DV = 48, not a multiple of 128
+    (dict(N=200), 1),                         # hidden width not a multiple of 128
+    (dict(wo=ctypes.c_void_p(0x10008)), 1),   # misaligned weights
+    (dict(wsb=1024), 1),                      # workspace too small
+])
+def test_mla_tail_rejects(kw, status):
+    lib = binding.load_library()
+    assert tail(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_mla_tail_workspace_bytes():
+    # u (bf16 [T, H*DV], rounded up to 256 bytes) + fp32 partials of every K slice
+    n = attn.attn_mla_tail_workspace_bytes(16, 128, 512, 128, 7168)
+    assert n >= 16 * 128 * 128 * 2 + 16 * 7168 * 4
+    assert (n - 16 * 128 * 128 * 2) % (16 * 7168 * 4) == 0
+    assert attn.attn_mla_tail_workspace_bytes(0, 128, 512, 128, 7168) == 0
