@@ -89,7 +89,8 @@ struct TailArgs {
 
 struct TailPlan {
     int ks;           // K slices of the o-projection grid
-    int kslice;       // K rows per slice (a multiple of 128)
+    int kslice;       // K rows per slice (a multiple of 64)
+    bool wn;          // o-projection workgroups span 512 columns (waves on N) instead of splitting K
     size_t u_bytes;   // bf16 u [T, H * DV], rounded up to 256 bytes
     size_t ws_bytes;  // u + fp32 partials [ks, T, N]
 };
