@@ -155,6 +155,12 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, (ATTN_LDS void*)(reinterpret_cast<uintptr_t>(lds_base)), 16, 0, 0);
 }
 
+// The same copy with the non-temporal hint (cache-policy bit nt): for data read once, such as
+// a KV cache streamed by decode, so it does not displace reused lines from the caches.
+__device__ __forceinline__ void load_lds16_nt(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (ATTN_LDS void*)(reinterpret_cast<uintptr_t>(lds_base)), 16, 0, 2);
+}
+
 // Buffer resource (V#) over [base, base + bytes): offsets >= bytes are out of range.
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 make_buffer(const void* base, uint32_t bytes) {

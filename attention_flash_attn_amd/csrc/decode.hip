@@ -125,14 +125,15 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(SplitParams p) {
             }
         }
     };
-    // V rows of step k0 into stage st (swizzled 16-byte chunks)
+    // V rows of step k0 into stage st (swizzled 16-byte chunks), non-temporal: each row is read
+    // once (measured 9% faster at 64 sequences of up to 32K keys; the same hint on K was slower)
     auto vload = [&](int k0, int blkA, int blkB, int st) {
 #pragma unroll
         for (int s = 0; s < VSEG; ++s) {
             const int off = s * 1024 + lane * 16;
             const int r = off / VROW;
             const int c = ((off % VROW) >> 4) ^ swz<NCV, true>(r);
-            load_lds16(p.vc + row_off(k0, k0 + r, blkA, blkB) * DV + c * 8, vl + st * STAGE + s * 1024);
+            load_lds16_nt(p.vc + row_off(k0, k0 + r, blkA, blkB) * DV + c * 8, vl + st * STAGE + s * 1024);
         }
     };
     constexpr int LOADS_PER_STEP = 2 * KQ + VSEG;  // vector-memory instructions issued per step
