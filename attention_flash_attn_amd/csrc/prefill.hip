@@ -33,8 +33,9 @@
 //    is an exact convex combination of V rows up to fp32 accumulation.
 //  * Additive mask (optional, IEEE fp16 [MB, MH, Sq, stride], head h of batch b
 //    reading mask[b % MB][h % MH] as in the page's kernel), times the head's
-//    ALiBi slope, is added after the softcap; each lane reads its query row's
-//    entries for a tile with 8-byte buffer loads one tile ahead.
+//    ALiBi slope, is added after the softcap; each wave copies its 32 rows of a
+//    tile's mask into LDS with the tile's K/V copies (whole row segments per
+//    copy), and each lane reads its row's entries from there.
 //  * Causal: tiles past the workgroup's last visible key are never loaded, a
 //    wave skips tiles wholly above its diagonal, and only tiles crossing the
 //    diagonal or the end of the keys evaluate the mask. Workgroups are
@@ -68,9 +69,6 @@ struct PrefillParams {
     int q_type;  // 0 bf16, 1 fp32, 2 fp16
 };
 
-// 8-byte buffer load (4 fp16 mask entries); offsets past the resource read 0.
-extern "C" __device__ u32x2 llvm_amdgcn_raw_buffer_load_v2i32(i32x4 rsrc, int voffset, int soffset,
-                                                              int aux) __asm("llvm.amdgcn.raw.buffer.load.v2i32");
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
@@ -112,7 +110,9 @@ void prefill_kernel(PrefillParams p) {
     static_assert(DK % 16 == 0 && DV % 16 == 0 && BN % 32 == 0, "tile shape");
     static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "tile must split into 1 KB segments");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    // additive mask (ADDM): each wave's 32 query rows x BN keys of fp16 per stage
+    constexpr int MT = 32 * BN * 2;
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + (ADDM ? 2 * NW * MT : 0)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -217,19 +217,21 @@ void prefill_kernel(PrefillParams p) {
     float l_run = 0.f;        // this lane's share of the running sum (its half of each key block)
     const int lim = CAUSAL ? min(p.Sk - 1, qi + shift) : p.Sk - 1;  // last visible key of this row
 
-    // additive mask: this lane's query row of slab mask[b % MB][h % MH]; rows past Sq read row Sq-1
+    // additive mask: the wave's 32 query rows of slab mask[b % MB][h % MH] (rows past Sq read
+    // row Sq-1), copied per tile into the wave's own LDS region with the K/V copies of the
+    // tile (16-byte chunks, 8 rows per 1 KB copy, so each copy reads whole row segments).
+    // Chunk c of row r sits at slot c ^ mswz(r): a lane's 8-byte read of its row then
+    // shares a bank pair with at most one other lane of its half-wave.
     i32x4 mrsrc = {0, 0, 0, 0};
-    uint32_t mrow_off = 0;
     float ms2 = 0.f;  // slope * log2 e
-    // entries of tile t+1 load during tile t (MPF), except at head dims whose registers are full,
-    // where tile t's entries load right after its barrier (ahead of the next tile's copies)
-    constexpr bool MPF = ADDM && (DK < 192 || OCC == 1);
-    u32x2 mcur[KB][4], mnext[KB][4];
+    constexpr int MCH = BN * 2 / 16;       // 16-byte chunks per mask row of a tile
+    constexpr int MRPI = 1024 / (BN * 2);  // mask rows per 1 KB copy
+    auto mswz = [](int r) { return (r >> 1) & (MCH - 1); };
+    char* const mstage = smem + 2 * STAGE + wave * MT;  // + stage * NW * MT
     if constexpr (ADDM) {
         const size_t slab = (size_t)p.Sq * (size_t)p.mask_stride;
         const uint16_t* mb = p.mask + ((size_t)(b % p.mask_batch) * p.mask_heads + (h % p.mask_heads)) * slab;
         mrsrc = make_buffer(mb, (uint32_t)(slab * 2));
-        mrow_off = (uint32_t)((size_t)min(qi, p.Sq - 1) * (size_t)p.mask_stride * 2);
         // ALiBi slope: m0^(h+1) below n_head_log2, else m1^(2(h - n_head_log2) + 1), with
         // m0 = 2^(-max_bias / n_head_log2) and m1 = 2^(-max_bias / (2 n_head_log2)); 1 when max_bias = 0
         const float e = h < p.n_head_log2 ? -(float)(h + 1) * p.max_bias / (float)p.n_head_log2
@@ -237,25 +239,28 @@ void prefill_kernel(PrefillParams p) {
                                                 (2.f * (float)p.n_head_log2);
         ms2 = exp2_fast(e) * kLog2e;
     }
-    auto mload = [&](int t, u32x2 (&m)[KB][4]) {
+    // mask entries of tile t into stage st (keys past the slab end are not copied; they
+    // only occur in the masked last tile, where those keys are excluded)
+    auto mload = [&](int t, int st) {
+        if constexpr (ADDM) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int key = t * BN + kb * 32 + g4 * 8 + half * 4;
-                m[kb][g4] = llvm_amdgcn_raw_buffer_load_v2i32(mrsrc, (int)(mrow_off + (uint32_t)key * 2u), 0, 0);
+            for (int j = 0; j < MT / 1024; ++j) {
+                const int r = j * MRPI + lane / MCH;
+                const int c = (lane % MCH) ^ mswz(r);
+                const uint32_t off = (uint32_t)((size_t)min(q0 + r, p.Sq - 1) * (size_t)p.mask_stride * 2) +
+                                     (uint32_t)(t * BN * 2 + c * 16);
+                buffer_load_lds16(mrsrc, off, mstage + st * NW * MT + j * 1024);
             }
+        }
     };
-    if constexpr (MPF) {
-        if (ntiles > 0) mload(0, mcur);
-    }
+    if (ntiles > 0) mload(0, 0);
     // per-lane LDS byte offsets: K row col (both key blocks), 16-byte half `half`;
     // V^T rows half*4 + (lane&15)/4 of a 4-row transposing block, column
     // ((lane>>4)&1)*16 + (lane&3)*4 of a 32-column block
     const int kofs = col * 32 + ((half ^ ((col >> 3) & 1)) << 4);
     const int vofs = (half * 4 + ((lane & 15) >> 2)) * 64 + (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
 
-    auto tile = [&](const char* kt, const char* vt, int key0, auto mask_tag) {
+    auto tile = [&](const char* kt, const char* vt, const char* mt, int key0, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // S^T = K Q^T; K fragments are read from LDS PF steps ahead of their MFMA
         constexpr int NQK = KB * KK;
@@ -295,7 +300,7 @@ void prefill_kernel(PrefillParams p) {
             for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const f16x4 mv = __builtin_bit_cast(f16x4, mcur[kb][g4]);
+                    const f16x4 mv = *(const f16x4*)(mt + col * (BN * 2) + (((kb * 4 + g4) ^ mswz(col)) << 4) + half * 8);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = g4 * 4 + e;
@@ -379,37 +384,26 @@ void prefill_kernel(PrefillParams p) {
     if (CAUSAL) t_full = min(t_full, max(0, (qt * BM + shift + 1) / BN));
     t_full = min(t_full, ntiles);
     auto step = [&](int t) {
-        wait_vmem();       // this wave's loads of tile t (and its mask entries) have landed
+        wait_vmem();       // this wave's copies of tile t (K/V and its mask rows) have landed
         __syncthreads();   // ... and every other wave's; stage (t+1)&1 is free again
-        if constexpr (ADDM && !MPF) mload(t, mcur);
         if (t + 1 < ntiles) {
             issue(t + 1, (t + 1) & 1);
-            if constexpr (MPF) mload(t + 1, mnext);
+            mload(t + 1, (t + 1) & 1);
         }
         __builtin_amdgcn_sched_barrier(0);
-    };
-    auto next_mask = [&]() {
-        if constexpr (MPF) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) mcur[kb][g4] = mnext[kb][g4];
-        }
     };
 #pragma clang loop unroll(disable)
     for (int t = 0; t < t_full; ++t) {
         step(t);
         const char* kt = smem + (t & 1) * STAGE;
-        tile(kt, kt + K_BYTES, t * BN, std::false_type{});
-        next_mask();
+        tile(kt, kt + K_BYTES, mstage + (t & 1) * NW * MT, t * BN, std::false_type{});
     }
 #pragma clang loop unroll(disable)
     for (int t = t_full; t < ntiles; ++t) {
         step(t);
         const char* kt = smem + (t & 1) * STAGE;
         const bool skip = CAUSAL && (t * BN > q0 + 31 + shift);  // wave-uniform
-        if (!skip) tile(kt, kt + K_BYTES, t * BN, std::true_type{});
-        next_mask();
+        if (!skip) tile(kt, kt + K_BYTES, mstage + (t & 1) * NW * MT, t * BN, std::true_type{});
     }
 
     // epilogue: sinks, normalisation, store
