@@ -525,7 +525,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         case 96096: return launch_inst<96, 96, 64, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
         case 128128: return launch_inst<128, 128, ATTN_D128_CFG>(p, kv_f16, causal, softcap, of32, stream);
         case 192192: return launch_inst<192, 192, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
-        case 256256: return launch_inst<256, 256, ATTN_D256_CFG, 32, 4, 1>(p, kv_f16, causal, softcap, of32, stream);
+        case 256256: return launch_inst<256, 256, ATTN_D256_CFG>(p, kv_f16, causal, softcap, of32, stream);
         case 192128: return launch_inst<192, 128, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
         default: return hipErrorInvalidValue;
     }
