@@ -17,7 +17,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libattn.so")
-SOURCES = ["prefill.hip", "decode.hip", "dequant.hip", "mla_tail.hip", "abi.cpp"]
+SOURCES = ["prefill.hip", "prefill_d256.hip", "decode.hip", "dequant.hip", "mla_tail.hip", "abi.cpp"]
+# per-source compiler options: the head-dim-256 prefill kernels use the max-ILP
+# machine scheduler (measured faster there, slower at head dim 128)
+EXTRA_FLAGS = {"prefill_d256.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 ARCH = "gfx950"
 
 
@@ -37,7 +40,7 @@ def common_flags():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile of %s failed:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -31,6 +31,8 @@ struct PrefillArgs {
 // Returns false if (dk, dv) has no compiled instance.
 bool prefill_supported(int dk, int dv);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Head dim (256, 256), built in its own translation unit (called by launch_prefill).
+hipError_t launch_prefill_d256(const PrefillArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
     const void* q;
