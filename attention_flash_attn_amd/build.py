@@ -18,9 +18,10 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libattn.so")
 SOURCES = ["prefill.hip", "prefill_d256.hip", "decode.hip", "dequant.hip", "mla_tail.hip", "abi.cpp"]
-# per-source compiler options: the head-dim-256 prefill kernels use the max-ILP
-# machine scheduler (measured faster there, slower at head dim 128)
-EXTRA_FLAGS = {"prefill_d256.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# per-source compiler options: the head-dim-256 prefill kernels and the MLA tail use
+# the max-ILP machine scheduler (measured 3% and 2% faster; 4% slower for head dim 128)
+_MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+EXTRA_FLAGS = {"prefill_d256.hip": _MAX_ILP, "mla_tail.hip": _MAX_ILP}
 ARCH = "gfx950"
 
 
