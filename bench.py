@@ -289,9 +289,11 @@ def main():
             def run(q=q, k=k, v=v, o=o, sk=sk, c=c):
                 binding.attn_prefill_fwd(q, k, v, o, None, scale=c["scale"], causal=c["causal"],
                                          softcap=c["softcap"], sinks=sk)
-            for _ in range(20):  # steady clocks before timing
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 0.1:  # at least 100 ms of warm work: steady clocks
                 run()
-            reps = 20
+                torch.cuda.synchronize()
+            reps = 50
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record(stream)
