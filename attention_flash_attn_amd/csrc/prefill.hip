@@ -59,7 +59,7 @@ struct PrefillParams {
     float c_score;  // scale * log2 e                (softcap off)
     float c_tanh;   // 2 * scale / softcap * log2 e  (softcap on: exponent of e^{2y})
     float c_cap;    // softcap * log2 e
-    int xcd_remap;  // B * Hq is a multiple of 8
+    int xcd_remap;  // 1: B * Hq is a multiple of 8; 2: also B * Hkv (grouped query heads)
     // additive mask (fp16 bits) and ALiBi
     const uint16_t* __restrict__ mask;
     long long mask_stride;  // elements between query rows
@@ -121,10 +121,18 @@ void prefill_kernel(PrefillParams p) {
     const int col = lane & 31;
 
     // workgroup -> (query tile, head, batch): heaviest tiles first; with
-    // xcd_remap, XCD x (= blockIdx % 8) works on heads x, x+8, ...
+    // xcd_remap 1, XCD x (= blockIdx % 8) works on heads x, x+8, ...; with 2, on
+    // the KV groups x, x+8, ... (every query head of a group on one XCD, whose L2
+    // then serves the group's K/V to all of them)
     const int HB = p.Hq * p.B;
     int qt, hb;
-    if (p.xcd_remap) {
+    if (p.xcd_remap == 2) {
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3, per = HB >> 3;
+        qt = p.nqt - 1 - j / per;
+        const int r = j % per, G = p.group;
+        const int kg = x + 8 * (r / G);
+        hb = (kg / p.Hkv) * p.Hq + (kg % p.Hkv) * G + r % G;
+    } else if (p.xcd_remap) {
         const int x = blockIdx.x & 7, j = blockIdx.x >> 3, per = HB >> 3;
         qt = p.nqt - 1 - j / per;
         hb = x + 8 * (j % per);
@@ -498,6 +506,9 @@ PrefillParams make_params(const PrefillArgs& a) {
     p.c_tanh = softcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
     p.c_cap = a.softcap * kLog2e;
     p.xcd_remap = ((a.B * a.Hq) % 8) == 0;
+    // grouped query heads per XCD: measured 3.5% faster for causal GQA at d=256, 2.4% slower
+    // without the causal mask
+    if (a.causal && a.Hq != a.Hkv && ((a.B * a.Hkv) % 8) == 0) p.xcd_remap = 2;
     p.mask = (const uint16_t*)a.mask;
     p.mask_stride = a.mask_stride;
     p.mask_batch = a.mask_batch;

@@ -72,6 +72,12 @@ def test_gqa_and_tails(Hq, Hkv):
     check_case(1, 300, 257, Hq, Hkv, 128, 128, causal=False, o_dtype="bf16", seed=103)
 
 
+def test_causal_gqa_grouped_xcd_order():
+    """Causal GQA with B * Hkv a multiple of 8: workgroups are ordered by KV group."""
+    check_case(2, 600, 600, 16, 4, 128, 128, causal=True, o_dtype="bf16", seed=115)
+    check_case(1, 300, 300, 16, 8, 256, 256, causal=True, sinks=True, o_dtype="f32", std=0.5, seed=116)
+
+
 def test_causal_rectangular_bottom_right():
     check_case(1, 70, 333, 2, 1, 128, 128, causal=True, o_dtype="f32", seed=104)   # Sq < Sk
     check_case(1, 200, 60, 2, 1, 64, 64, causal=True, o_dtype="f32", seed=105)     # Sq > Sk: empty rows
