@@ -82,8 +82,8 @@ def main():
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (the kernels shard over "
-              "(batch, KV head) with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (the kernels would shard "
+              "over (batch, KV head) with no exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
