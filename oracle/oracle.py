@@ -32,7 +32,7 @@ Sources (page titles and sections):
     causal mask driven by each selected key's absolute position against the
     token's own position.
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
   * softcap: x <- softcap * tanh(x / softcap); 0 disables it.
   * causal prefill with Sq != Sk is bottom-right aligned: query i sits at
     absolute position Sk - Sq + i and sees keys j <= Sk - Sq + i.
