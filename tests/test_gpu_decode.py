@@ -62,6 +62,12 @@ def test_paged_gqa_ratios_and_features():
     check_paged(2, 8, 1, 128, 128, 0, 5, o_dtype="f32", seed=205, lens=[0, 5])        # empty sequence
 
 
+def test_paged_causal_more_queries_than_keys():
+    """Causal decode with Sq > L_b: query i sits at L_b - Sq + i, so the first Sq - L_b rows
+    see no key and are 0 (the prefill's bottom-right alignment and empty-row rule)."""
+    check_paged(3, 16, 2, 128, 128, 2, 40, Sq=6, causal=True, o_dtype="f32", seed=207, lens=[2, 6, 40])
+
+
 def test_paged_block_permutation_invariance():
     case = synth.paged_case(206, 3, 8, 1, 128, 128, 100, 1000)
     o1 = run_paged(case, 0.09, False, 0.0, "f32", 1000)
