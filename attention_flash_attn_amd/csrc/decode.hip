@@ -586,13 +586,16 @@ struct CombineParams {
     int Sq, Hq, n_split, split_len, dv;
 };
 
-// One wavefront per output row (b, query, head). Each lane owns 4 columns; the
-// splits are read 8 at a time (indices clamped, weights of missing splits 0) so
-// that many loads are in flight. Rows narrower than 256 columns put the spare
-// lanes on other splits and add the phases up in LDS.
+// One wavefront per output row (b, query, head). Each lane owns 4 columns (two
+// 4-column groups for rows of 512 columns); rows narrower than 256 columns put
+// the spare lanes on other splits and add the phases up in LDS. The first 8
+// splits of the lane's columns are loaded before the split maxima are read, so
+// the row costs one memory latency rather than two; further splits follow 8 at
+// a time (indices clamped, values of missing splits zeroed).
 template <bool OF32>
 __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
     constexpr int U = 8;
+    constexpr int CL = 2;  // column groups per lane at most (dv <= 512)
     const int lane = threadIdx.x;
     const size_t row = blockIdx.x;
     const int h = (int)(row % p.Hq);
@@ -603,6 +606,29 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
         nv = min(p.n_split, (L + p.split_len - 1) / p.split_len);
     }
     const float* ml = p.ws_ml + row * p.n_split * 2;
+    const float* ob = p.ws_o + row * p.n_split * p.dv;
+    const int ncg = p.dv >> 2;  // 4-column groups
+    // lane -> column groups c0 (+64) and split phase ph of G
+    const int G = ncg >= 64 ? 1 : 64 / ncg;
+    const int ncl = ncg >= 64 ? ncg / 64 : 1;
+    const int c0 = ncg >= 64 ? lane : lane % ncg, ph = ncg >= 64 ? 0 : lane / ncg;
+    const bool active = ph < G;
+
+    auto load_batch = [&](int s0, f32x4 (&x)[CL][U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * G;
+            const int sc = max(min(s, nv - 1), 0);
+#pragma unroll
+            for (int g = 0; g < CL; ++g) {
+                x[g][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (active && g < ncl) x[g][u] = *(const f32x4*)(ob + (size_t)sc * p.dv + (c0 + 64 * g) * 4);
+            }
+        }
+    };
+    f32x4 x[CL][U];
+    load_batch(ph, x);
+
     float M = -INFINITY;
     for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
 #pragma unroll
@@ -617,50 +643,44 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
     for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
     if (has_sink) l += exp2_fast(sink2 - Mu);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const float* ob = p.ws_o + row * p.n_split * p.dv;
-    const int ncg = p.dv >> 2;  // 4-column groups
 
-    auto store = [&](int c, f32x4 acc) {
-        acc *= inv;
+    // sum over the splits s = ph, ph + G, ... (< nv) of e^{m_s - M} O_s
+    f32x4 acc[CL];
+#pragma unroll
+    for (int g = 0; g < CL; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = ph; s0 < nv; s0 += U * G) {
+        if (s0 != ph) load_batch(s0, x);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = s0 + u * G;
+            const float w = exp2_fast(ml[2 * max(min(s, nv - 1), 0)] - Mu);
+#pragma unroll
+            for (int g = 0; g < CL; ++g)
+                if (s < nv) acc[g] += w * x[g][u];
+        }
+    }
+
+    auto store = [&](int c, f32x4 a) {
+        a *= inv;
         if constexpr (OF32) {
-            *(f32x4*)((float*)p.o + row * p.dv + c * 4) = acc;
+            *(f32x4*)((float*)p.o + row * p.dv + c * 4) = a;
         } else {
             *(u32x2*)((uint16_t*)p.o + row * p.dv + c * 4) =
-                u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+                u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
         }
     };
-    // sum over splits s = s_first, s_first + stride, ... (< nv) of w_s * O_s[columns 4c..4c+3]
-    auto accumulate = [&](int c, int s_first, int stride) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = s_first; s0 < nv; s0 += U * stride) {
-            f32x4 x[U];
-            float w[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int s = s0 + u * stride;
-                const int sc = min(s, nv - 1);
-                w[u] = s < nv ? exp2_fast(ml[2 * sc] - Mu) : 0.f;
-                x[u] = *(const f32x4*)(ob + (size_t)sc * p.dv + c * 4);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc += w[u] * x[u];
-        }
-        return acc;
-    };
-
     if (ncg >= 64) {
-        for (int c = lane; c < ncg; c += 64) store(c, accumulate(c, 0, 1));
-    } else {
+#pragma unroll
+        for (int g = 0; g < CL; ++g)
+            if (g < ncl) store(c0 + 64 * g, acc[g]);
+    } else {  // lanes of phase >= G (when 64 % ncg != 0) only add zeros
         __shared__ f32x4 red[64];
-        const int G = 64 / ncg;  // split phases
-        const int c = lane % ncg, ph = lane / ncg;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (ph < G) acc = accumulate(c, ph, G);
-        red[lane] = acc;
+        red[lane] = acc[0];
         __syncthreads();
         if (ph == 0) {
-            for (int g = 1; g < G; ++g) acc += red[g * ncg + c];
-            store(c, acc);
+            f32x4 a = acc[0];
+            for (int q = 1; q < G; ++q) a += red[q * ncg + c0];
+            store(c0, a);
         }
     }
 }

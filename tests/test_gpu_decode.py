@@ -180,6 +180,14 @@ def test_gathered_current_row():
     check_gathered(3, 128, 4096, 300, with_cur=True, v_offset=64, softcap=30.0, sinks=True, seed=323)
 
 
+def test_gathered_long_selection():
+    """4096 and more selected rows take 512-key splits; the last split holds a full index
+    table of 512 rows plus the current row."""
+    check_gathered(2, 64, 16384, 4096, with_cur=True, seed=325)                   # 8 full splits + 1 row
+    check_gathered(2, 32, 16384, 5000, future=64, o_dtype="bf16", seed=326)      # ragged tenth split
+    check_gathered(1, 64, 16384, 4608, with_cur=True, v_offset=64, seed=327)     # separate value rows
+
+
 def test_gathered_only_current_row_live():
     """Every selected key lies after the token: the output is the current row's value."""
     o, ro = check_gathered(3, 64, 2048, 96, with_cur=True, future=96, seed=324)
