@@ -188,6 +188,32 @@ def test_gathered_long_selection():
     check_gathered(1, 64, 16384, 4608, with_cur=True, v_offset=64, seed=327)     # separate value rows
 
 
+def test_gathered_separate_value_rows():
+    """Value rows in an array of their own (same row stride as the key rows), with and
+    without the token's own rows."""
+    for T, Hq, n_sel, cur, seed in [(3, 64, 300, False, 328), (2, 128, 700, True, 329)]:
+        print("gathered separate value rows T=%d Hq=%d n_sel=%d cur=%d" % (T, Hq, n_sel, cur), flush=True)
+        case = synth.gathered_case(seed, T, Hq, 576, 512, 4096, n_sel, row_dim=576, future_keys=16)
+        vrows = synth.normal_bf16(seed, 7, (4096, 576))
+        kv, q = dev_bf16(case["kv"]), dev_bf16(case["q"]).view(T, 1, Hq, 576)
+        vd = dev_bf16(vrows)
+        o = torch.empty((T, 1, Hq, 512), device="cuda", dtype=torch.float32)
+        ws = torch.empty(binding.attn_decode_workspace_bytes(T, Hq, 1, 1, n_sel, 576, 512), device="cuda",
+                         dtype=torch.uint8)
+        kcur = synth.normal_bf16(seed, 9, (T, 576)) if cur else None
+        vcur = synth.normal_bf16(seed, 10, (T, 576)) if cur else None
+        binding.attn_decode_fwd(q, kv, vd[:, :512], o, ws, scale=1 / 24, Sk_max=n_sel, causal=True,
+                                row_index=dev(case["row_index"]), key_pos=dev(case["key_pos"]),
+                                q_pos=dev(case["q_pos"]), dk=576, dv=512,
+                                k_cur=None if kcur is None else dev_bf16(kcur),
+                                v_cur=None if vcur is None else dev_bf16(vcur)[:, :512])
+        torch.cuda.synchronize()
+        ro, _ = oracle.decode_gathered(case["q"], case["kv"], vrows[:, :512], case["row_index"], case["key_pos"],
+                                       case["q_pos"], 1 / 24, causal=True, k_cur=kcur,
+                                       v_cur=None if vcur is None else vcur[:, :512])
+        check_close(host(o[:, 0]), ro, "f32", "gathered decode, separate value rows")
+
+
 def test_gathered_only_current_row_live():
     """Every selected key lies after the token: the output is the current row's value."""
     o, ro = check_gathered(3, 64, 2048, 96, with_cur=True, future=96, seed=324)
