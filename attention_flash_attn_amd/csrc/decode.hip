@@ -286,10 +286,15 @@ void decode_paged_split_kernel(SplitParams p) {
 // Stage layout: 32 rows at a pitch of one row (DK*2 bytes, 128 mod 256), so
 // each 1 KB direct load reads contiguous global memory. Row r stores its
 // logical 16-byte chunk c at c ^ sw(r) (sw(r) < 8 permutes within aligned
-// groups of 8 chunks); with that swizzle both reads are conflict-free and
-// every address is one of a few per-lane bases plus an immediate:
+// groups of 8 chunks), and every address is one of a few per-lane bases plus
+// an immediate:
 //   K operand: a 128-bit read of one chunk by 16 consecutive rows;
 //   V^T operand: a transposing read of 4 consecutive rows x 32 bytes.
+// The LDS serves a 128-bit read to lanes 0-7 with 32-39 in one cycle (then
+// 8-15 with 40-47, ...) and a 64-bit read to 32 consecutive lanes; under that
+// grouping (measured with the bank-conflict counter on these exact address
+// patterns) sw(r) = r1 | (r1^r2) << 1 | (r2^r3) << 2 makes both reads
+// conflict-free. (A plain bit permutation left the K reads 2-way conflicted.)
 struct GatherParams {
     const void* __restrict__ q;  // bf16, fp32 or fp16 (q_type)
     const uint16_t* __restrict__ kc;
@@ -407,7 +412,7 @@ void decode_gathered_split_kernel(GatherParams p) {
     }
 
     // row r stores logical chunk c at chunk c ^ sw(r) (within aligned groups of 8)
-    auto sw = [](int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); };
+    auto sw = [](int r) { return ((r >> 1) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 2); };
     // Rows of step i into stage st: wave w fills 1 KB segments w, w+NW, ... All row offsets
     // of the step are read from LDS before the first copy is issued (a copy writes LDS, so a
     // later table read could not be moved ahead of it).
