@@ -181,11 +181,14 @@ def test_gathered_current_row():
 
 
 def test_gathered_long_selection():
-    """4096 and more selected rows take 512-key splits; the last split holds a full index
-    table of 512 rows plus the current row."""
+    """4096 and more selected rows take 512-key splits, 16384 and more 1024-key splits; the
+    last split can hold a full index table plus the current row."""
     check_gathered(2, 64, 16384, 4096, with_cur=True, seed=325)                   # 8 full splits + 1 row
     check_gathered(2, 32, 16384, 5000, future=64, o_dtype="bf16", seed=326)      # ragged tenth split
     check_gathered(1, 64, 16384, 4608, with_cur=True, v_offset=64, seed=327)     # separate value rows
+    # 16384 and more take 1024-key splits: full index tables of 1024 rows (+ the current row)
+    check_gathered(2, 32, 32768, 16384, with_cur=True, seed=330)
+    check_gathered(1, 20, 32768, 17000, future=32, o_dtype="bf16", seed=331)
 
 
 def test_gathered_separate_value_rows():
