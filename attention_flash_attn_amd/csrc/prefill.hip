@@ -551,8 +551,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         case 64064: return launch_inst<64, 64, 64, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
         case 96096: return launch_inst<96, 96, 64, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
         case 128128: return launch_inst<128, 128, ATTN_D128_CFG>(p, kv_f16, causal, softcap, of32, stream);
-        case 192192: return launch_inst<192, 192, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
-        case 192128: return launch_inst<192, 128, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
+        // 64 keys x 8 waves without a mask (7-8% faster than 32 x 4 at B=2, H=32, 4096^2
+        // causal); the masked instances keep 32 x 4
+        case 192192: return launch_inst<192, 192, 64, 8, 2, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
+        case 192128: return launch_inst<192, 128, 64, 8, 2, 32, 4, 2>(p, kv_f16, causal, softcap, of32, stream);
         default: return hipErrorInvalidValue;
     }
 }
