@@ -37,9 +37,9 @@ METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM pe
 # scaled x2, write x1 against a 1 GiB plain copy; see profiles/hbm_traffic_bench.md), valid
 # only while the kernel sources hash to the values they were measured on.
 MEASURED_TRAFFIC = {
-    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp"), "sha256_16": "8ecb09e002dfe0fe", "bytes": 591112395},
-    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp"), "sha256_16": "0b13abd56c833c69", "bytes": 5035275792},
-    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp"), "sha256_16": "0b13abd56c833c69", "bytes": 123640177},
+    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp"), "sha256_16": "8979e4b4e48eb1a4", "bytes": 611531134},
+    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp"), "sha256_16": "0b13abd56c833c69", "bytes": 5035253486},
+    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp"), "sha256_16": "0b13abd56c833c69", "bytes": 123639588},
 }
 
 
