@@ -74,6 +74,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle", type=float, default=0.2,
+                    help="seconds of untimed steps run before the warm-up steps, so the GPU clock reaches its "
+                         "steady state whatever --warmup is (0 = none); reported as settle_s")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-other", action="store_true", help="skip the extra workloads")
     ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) pairs in the CPU sample")
@@ -145,6 +148,15 @@ def main():
         log("calibration copy: 1 GiB in %.1f us (%.0f GB/s read+write)" %
             (c0.elapsed_time(c1) * 1e3, 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9))
         del src, dst
+    # clock settle: under this load the GPU clock needs ~0.1 s to reach its steady state, longer
+    # than a few warm-up steps take, so full steps run untimed for a fixed time first
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(10):
+            prefill()
+            decode()
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         prefill()
         decode()
@@ -189,6 +201,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_s": round(settle_s, 3),
         "ms_per_step": round(wall / K * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
