@@ -52,6 +52,16 @@ attn_status check_dtypes(int q_dtype, int kv_dtype) {
     return ATTN_OK;
 }
 
+// Launch-size limits of a decode call that hold in both modes: B and the key-split count
+// are grid dimensions of the split kernels (at most 65535 each), and the combine runs one
+// 64-thread workgroup per output row in a grid dimension of fewer than 2^32 threads. Within
+// them the workspace size cannot overflow. Returns nullptr when the shape fits.
+const char* decode_too_large(int B, const attn::DecodePlan& pl) {
+    if (B > 65535 || pl.n_split > 65535) return "B and the key-split count must each be at most 65535";
+    if (pl.n_rows > (int64_t(1) << 26) - 1) return "B * Sq * Hq must be under 2^26 output rows";
+    return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,9 +107,11 @@ static attn_status prefill_impl(const void* q, int q_dtype, const void* k, const
         return fail(ATTN_ERR_INVALID_ARG, "max_bias must be finite and >= 0");
     if (!attn::prefill_supported(dk, dv))
         return fail(ATTN_ERR_UNSUPPORTED, "prefill (dk, dv) = (%d, %d) is not built", dk, dv);
-    const double rows = (double)B * Sq * Hq;
-    if ((double)B * ((Sq + 127) / 128) * Hq > 2147483647.0 || rows * dv > 9.0e18)
-        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch");
+    // one workgroup of 64 * NW threads per 32 * NW query rows (NW = 4 or 8) of one (head, batch
+    // entry): the 1-D grid holds at most (ceil(Sq / 128) + 1) * 256 threads per (head, batch
+    // entry), and a grid dimension holds fewer than 2^32 threads
+    if ((double)B * Hq * ((Sq + 127) / 128 + 1) * 256.0 > 4294967295.0)
+        return fail(ATTN_ERR_UNSUPPORTED, "problem too large for one launch (B * Hq * Sq too large)");
     if ((double)Sk * Hkv * (dk > dv ? dk : dv) * 2.0 >= 4294967296.0)
         return fail(ATTN_ERR_UNSUPPORTED, "K or V of one batch entry must be under 4 GiB");
 
@@ -151,7 +163,8 @@ attn_status attn_prefill_fwd_ex(const void* q, int q_dtype, const void* k, const
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk_max < 0 || dk <= 0 || dv <= 0 || Hq % Hkv != 0) return 0;
-    return attn::decode_plan(B, Hq, Hkv, Sq, Sk_max, dk, dv).ws_bytes;
+    const attn::DecodePlan pl = attn::decode_plan(B, Hq, Hkv, Sq, Sk_max, dk, dv);
+    return decode_too_large(B, pl) ? 0 : pl.ws_bytes;
 }
 
 attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype,
@@ -200,9 +213,15 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
         return fail(ATTN_ERR_UNSUPPORTED, "%s decode (dk, dv) = (%d, %d) is not built", gathered ? "gathered" : "paged",
                     dk, dv);
     const attn::DecodePlan pl = attn::decode_plan(B, Hq, Hkv, Sq, Sk_max, dk, dv);
-    if (B > 65535 || pl.n_split > 65535)
-        return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large (B = %d, %d key splits; at most 65535 each)", B,
-                    pl.n_split);
+    if (const char* why = decode_too_large(B, pl))
+        return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large (B = %d, Hq = %d, Sq = %d, %d key splits): %s", B, Hq,
+                    Sq, pl.n_split, why);
+    // the paged kernel's first grid dimension holds Hkv * (16-column query groups at most) wavefronts,
+    // the gathered kernel's second one the 64-head groups
+    if (paged && (int64_t)Hkv * (((int64_t)Sq * (Hq / Hkv) + 15) / 16) > (int64_t(1) << 26) - 1)
+        return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large: Hkv * Sq * (Hq / Hkv) / 16 must be under 2^26");
+    if (gathered && (Hq + 63) / 64 > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large: gathered mode takes at most 65535 * 64 heads");
     if (!workspace || workspace_bytes < pl.ws_bytes)
         return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", pl.ws_bytes, workspace_bytes);
     if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -249,7 +268,9 @@ attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blo
     if (n_blocks == 0) return ok();
     if (!src || !dst) return fail(ATTN_ERR_INVALID_ARG, "src and dst are required");
     if (!aligned16(src) || !aligned16(dst)) return fail(ATTN_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
-    if (n_blocks > ((int64_t)1 << 38)) return fail(ATTN_ERR_UNSUPPORTED, "too many blocks for one launch");
+    // one thread per block in a 1-D grid of fewer than 2^32 threads (256 per workgroup)
+    if (n_blocks > ((int64_t)1 << 32) - 256)
+        return fail(ATTN_ERR_UNSUPPORTED, "n_blocks above 2^32 - 256: too many blocks for one launch");
     hipError_t e = attn::launch_dequant(src, fmt, dst, (long long)n_blocks, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "dequant launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -274,6 +295,9 @@ attn_status attn_mla_tail(const void* o_lat, const void* w_absorb, const void* w
     if (K % 128 != 0) return fail(ATTN_ERR_INVALID_ARG, "H * DV (%lld) must be a multiple of 128", K);
     if (N % 128 != 0) return fail(ATTN_ERR_INVALID_ARG, "N (%d) must be a multiple of 128", N);
     if (N / 128 > 65535) return fail(ATTN_ERR_INVALID_ARG, "N (%d) exceeds 128 * 65535", N);
+    // the slice sum runs one thread per 4 outputs in a 1-D grid of fewer than 2^32 threads
+    if ((long long)T * N > (1LL << 34) - 256)
+        return fail(ATTN_ERR_INVALID_ARG, "T * N (%lld) exceeds 2^34 - 256", (long long)T * N);
     if (K > INT32_MAX / 2 || (long long)H * (DV / 16) > INT32_MAX)
         return fail(ATTN_ERR_INVALID_ARG, "H * DV (%lld) too large", K);
     if (!aligned16(o_lat) || !aligned16(w_absorb) || !aligned16(w_o) || !aligned16(y) || !aligned16(workspace))

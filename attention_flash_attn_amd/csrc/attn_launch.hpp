@@ -67,7 +67,7 @@ struct DecodeArgs {
 struct DecodePlan {
     int split_len;   // keys per split (multiple of the kernel's key tile)
     int n_split;     // ceil(Sk_max / split_len)
-    int n_rows;      // B * Sq * Hq output rows
+    int64_t n_rows;  // B * Sq * Hq output rows
     size_t ws_bytes; // partial O (fp32, dv per row per split) + (max, sum) per row per split
 };
 

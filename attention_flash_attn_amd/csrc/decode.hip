@@ -87,7 +87,7 @@ void decode_paged_split_kernel(SplitParams p) {
         const bool ok = colq < p.nq;
         const int si = ok ? colq / p.group : 0;
         const int h = g * p.group + (ok ? colq % p.group : 0);
-        const size_t qrow = ((size_t)(b * p.Sq + si) * p.Hq + h) * DK;
+        const size_t qrow = (((size_t)b * p.Sq + si) * p.Hq + h) * DK;
 #pragma unroll
         for (int kk = 0; kk < KQ; ++kk) {
             const int dk0 = kk * 32 + grp * 8;
@@ -260,7 +260,7 @@ void decode_paged_split_kernel(SplitParams p) {
         if (colq < p.nq) {
             const int si = colq / p.group;
             const int h = g * p.group + colq % p.group;
-            const size_t row = (size_t)(b * p.Sq + si) * p.Hq + h;
+            const size_t row = ((size_t)b * p.Sq + si) * p.Hq + h;
             const size_t slot = row * p.n_split + split;
             if (grp == 0) {
                 p.ws_ml[slot * 2] = m_run[cb];
@@ -782,7 +782,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
         pl.split_len = sl;
     }
     pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;
-    pl.n_rows = B * Sq * Hq;
+    pl.n_rows = (int64_t)B * Sq * Hq;
     pl.ws_bytes = (size_t)pl.n_rows * pl.n_split * ((size_t)dv + 2) * sizeof(float);
     pl.ws_bytes = (pl.ws_bytes + 255) & ~(size_t)255;
     return pl;

@@ -210,7 +210,7 @@ void prefill_kernel(PrefillParams p) {
     // this lane's Q fragments: row qi, chunks 2*kk + half
     bf16x8 qf[KK];
     {
-        const size_t qrow = ((size_t)(b * p.Sq + qi) * p.Hq + h) * DK;
+        const size_t qrow = (((size_t)b * p.Sq + qi) * p.Hq + h) * DK;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             qf[kk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
@@ -427,7 +427,7 @@ void prefill_kernel(PrefillParams p) {
         if (p.lse != nullptr && half == 0)
             p.lse[((size_t)b * p.Hq + h) * p.Sq + qi] =
                 den > 0.f ? (m2u + __builtin_amdgcn_logf(den)) * kLn2 : -INFINITY;
-        const size_t obase = ((size_t)(b * p.Sq + qi) * p.Hq + h) * DV;
+        const size_t obase = (((size_t)b * p.Sq + qi) * p.Hq + h) * DV;
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
 #pragma unroll

@@ -37,9 +37,9 @@ METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM pe
 # scaled x2, write x1 against a 1 GiB plain copy; see profiles/hbm_traffic_bench.md), valid
 # only while the kernel sources hash to the values they were measured on.
 MEASURED_TRAFFIC = {
-    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp", "../build.py"), "sha256_16": "d0b90f1ba0ae0421", "bytes": 617322240},
-    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "7f1811caa2637e01", "bytes": 5035284925},
-    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "7f1811caa2637e01", "bytes": 123607096},
+    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp", "../build.py"), "sha256_16": "0faed732a068c308", "bytes": 655551163},
+    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "3ad9e9d95ad13de5", "bytes": 5035247957},
+    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "3ad9e9d95ad13de5", "bytes": 123607473},
 }
 
 

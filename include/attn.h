@@ -65,7 +65,7 @@ extern "C" {
 typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1,   /* NULL required pointer, non-positive size, Hq % Hkv != 0, ... */
-    ATTN_ERR_UNSUPPORTED = 2,   /* legal but not built: (dk, dv) pair, mode combination */
+    ATTN_ERR_UNSUPPORTED = 2,   /* legal but not built: (dk, dv) pair, mode combination, sizes past a launch limit */
     ATTN_ERR_HIP = 3            /* a HIP launch failed */
 } attn_status;
 
@@ -96,6 +96,8 @@ const char* attn_last_error(void);
  *   scale multiplies the raw dot product (typically 1/sqrt(dk)); must be finite and > 0.
  *   causal 0/1; softcap >= 0 (0 = off); sinks optional fp32 [Hq].
  * Accumulation is fp32; the probabilities feed the second product as bf16.
+ * Launch-size limits (ATTN_ERR_UNSUPPORTED past them): K and V of one batch
+ * entry each under 4 GiB; B * Hq * (ceil(Sq / 128) + 1) * 256 under 2^32.
  */
 attn_status attn_prefill_fwd(const void* q, const void* k, const void* v,
                              void* o, int o_dtype, float* lse,
@@ -136,7 +138,8 @@ attn_status attn_prefill_fwd_ex(const void* q, int q_dtype, const void* k, const
  * Workspace (bytes) that attn_decode_fwd needs for these sizes: the split-KV
  * partial results (fp32 output rows plus running max and sum per split).
  * Sk_max is the largest sequence length (paged mode) or n_sel (gathered mode).
- * Returns 0 for sizes that attn_decode_fwd would reject.
+ * Returns 0 for sizes that attn_decode_fwd would reject in either mode (invalid,
+ * or past the mode-independent launch-size limits below).
  */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv);
 
@@ -145,8 +148,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  * case) against a KV cache read in one of two modes. The keys are split into
  * fixed-size ranges processed in parallel, then merged by log-sum-exp. The
  * range length (256..2048 keys) depends only on the sizes passed here and to
- * attn_decode_workspace_bytes; B and the number of ranges must not exceed
- * 65535 (ATTN_ERR_UNSUPPORTED otherwise).
+ * attn_decode_workspace_bytes. Launch-size limits (ATTN_ERR_UNSUPPORTED past
+ * them): B and the number of ranges at most 65535 each; B * Sq * Hq under 2^26
+ * output rows; paged mode Hkv * ceil(Sq * (Hq / Hkv) / 16) under 2^26;
+ * gathered mode Hq at most 65535 * 64.
  *
  *   q   [B, Sq, Hq, dk] contiguous, of type q_dtype (bf16, fp16 or fp32);
  *   caches of type kv_dtype (bf16 or fp16);   o [B, Sq, Hq, dv] of type o_dtype.
@@ -211,6 +216,8 @@ typedef enum attn_qfmt {
  * call the attention entry points with kv_dtype = ATTN_F16). d * q is exact in
  * fp32 and rounded once to fp16 (nearest even). src and dst are device
  * buffers, 16-byte aligned, not overlapping; n_blocks = 0 does nothing.
+ * One thread expands one block: n_blocks above 2^32 - 256 (a grid of 2^32
+ * threads) gives ATTN_ERR_UNSUPPORTED.
  */
 attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blocks, void* stream);
 
@@ -228,7 +235,8 @@ attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blo
  *   y         [T, N] contiguous, element type y_dtype (ATTN_BF16 or ATTN_F32);
  *             bf16 results are rounded to nearest even from the fp32 sum.
  * Requirements: T, H >= 1; R a multiple of 128; DV a multiple of 16; K a
- * multiple of 128; N a multiple of 128 (at most 128 * 65535); every pointer
+ * multiple of 128; N a multiple of 128 (at most 128 * 65535); T * N at most
+ * 2^34 - 256 (the final sum runs one thread per 4 outputs); every pointer
  * 16-byte aligned; workspace (device, caller-owned, at least
  * attn_mla_tail_workspace_bytes(T, H, R, DV, N) bytes, 16-byte aligned) holds u
  * and the fp32 partial sums of the K slices; it is fully overwritten. The

@@ -67,6 +67,7 @@ def prefill(lib, **kw):
     (dict(dk=48, dv=48), 2),
     (dict(dk=128, dv=64), 2),
     (dict(dk=576, dv=512), 2),
+    (dict(B=65536, Hq=128, Sq=1024), 2),              # grid of more than 2^32 threads
 ])
 def test_prefill_rejects(kw, status):
     lib = binding.load_library()
@@ -128,6 +129,10 @@ def decode(lib, **kw):
     (dict(ws_bytes=16), 1),
     (dict(ws=None), 1),
     (dict(Sq=1 << 12, Hq=512, Hkv=1), 2),                   # 2^21 query columns per KV head
+    (dict(B=65536), 2),                                     # B is a grid dimension of at most 65535
+    (dict(B=1024, Hq=1 << 16, Hkv=1 << 16), 2),             # 2^26 output rows for the combine
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=576, dk=576, dv=512,
+          Hq=65536 * 64), 2),                               # 65536 groups of 64 heads
     (dict(kcur=FAKE, vcur=FAKE), 1),                        # current rows in paged mode
     (dict(qd=5), 1),                                        # unknown q dtype
     (dict(kvd=1), 1),                                       # fp32 caches are not an operand type
@@ -160,6 +165,10 @@ def test_workspace_bytes():
     assert n >= 16 * 128 * 8 * 514 * 4
     assert attn.attn_decode_workspace_bytes(0, 64, 8, 1, 100, 128, 128) == 0
     assert attn.attn_decode_workspace_bytes(2, 6, 4, 1, 100, 128, 128) == 0
+    # past the launch limits (2^26 output rows; B above 65535): no workspace size
+    assert attn.attn_decode_workspace_bytes(1024, 1 << 16, 1 << 16, 1, 100, 128, 128) == 0
+    assert attn.attn_decode_workspace_bytes(65536, 8, 8, 1, 100, 128, 128) == 0
+    assert attn.attn_decode_workspace_bytes(1024, (1 << 16) - 64, 1, 1, 100, 128, 128) > 0
 
 
 @pytest.mark.parametrize("fmt,src,dst,n,status", [
@@ -168,6 +177,7 @@ def test_workspace_bytes():
     (0, None, FAKE, 4, 1),
     (1, ctypes.c_void_p(0x10002), FAKE, 4, 1),                # misaligned source
     (0, FAKE, FAKE, 0, 0),                                    # nothing to do (no launch)
+    (0, FAKE, FAKE, (1 << 32) - 255, 2),                      # one thread per block: grid past 2^32 threads
 ])
 def test_dequant_rejects(fmt, src, dst, n, status):
     lib = binding.load_library()
@@ -192,6 +202,7 @@ def tail(lib, **kw):
     (dict(N=200), 1),                         # hidden width not a multiple of 128
     (dict(wo=ctypes.c_void_p(0x10008)), 1),   # misaligned weights
     (dict(wsb=1024), 1),                      # workspace too small
+    (dict(T=1 << 27), 1),                     # T * N = 2^35 outputs: final-sum grid past 2^32 threads
 ])
 def test_mla_tail_rejects(kw, status):
     lib = binding.load_library()
