@@ -113,18 +113,44 @@ void decode_paged_split_kernel(SplitParams p) {
         const int blk = (key - k0) < 16 ? blkA : blkB;
         return ((size_t)blk * p.Hkv + g) * bs + (key & (bs - 1));
     };
+    // Keys k0..k0+15 lie in block blkA and k0+16..k0+31 in blkB (k0 is a multiple of 32, blocks
+    // hold >= 16 keys, and a key clamped to L - 1 stays in its half's block). A K fragment row
+    // (kb*16 + c16), and a V segment when 16 rows fill whole 1 KB segments, therefore read one
+    // block: a wave-uniform (scalar) block base plus a 32-bit per-lane offset inside the block.
+    // The 32-column instance addresses this way: with 64-bit per-lane addresses it spilled 13
+    // registers, and each reload's full vector-memory wait also waited for the next step's
+    // loads (4 tokens x 8 heads at config 4: 1027 -> 978 us). The 16-column instances keep
+    // per-lane addresses, 3-4% faster at d = 128 and 192/128 on 1024..8192-key sequences.
+    constexpr bool SBASE = CB == 2;
+    auto kv_base = [&](const uint16_t* cache, int blk, int d) -> const char* {
+        return (const char*)(cache + ((size_t)blk * p.Hkv + g) * bs * d);
+    };
+    auto row_in_block = [&](int key) -> uint32_t { return (uint32_t)(min(key, L - 1) & (bs - 1)); };
     // K fragments of step k0: block kb, k-step kk: key k0 + kb*16 + c16, dk kk*32 + grp*8
     auto kload = [&](int k0, int blkA, int blkB, u32x4 (&kr)[2][KQ]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint16_t* r = p.kc + row_off(k0, k0 + kb * 16 + c16, blkA, blkB) * DK;
+            if constexpr (SBASE) {
+                const char* base = kv_base(p.kc, kb ? blkB : blkA, DK);
+                const uint32_t ro = row_in_block(k0 + kb * 16 + c16) * (DK * 2);  // bytes
 #pragma unroll
-            for (int kk = 0; kk < KQ; ++kk) {
-                const int dk0 = kk * 32 + grp * 8;
-                if (dk0 < DK)
-                    kr[kb][kk] = *(const u32x4*)(r + dk0);
-                else
-                    kr[kb][kk] = u32x4{0, 0, 0, 0};
+                for (int kk = 0; kk < KQ; ++kk) {
+                    const int dk0 = kk * 32 + grp * 8;
+                    if (dk0 < DK)
+                        kr[kb][kk] = *(const u32x4*)(base + (size_t)(ro + (uint32_t)(dk0 * 2)));
+                    else
+                        kr[kb][kk] = u32x4{0, 0, 0, 0};
+                }
+            } else {
+                const uint16_t* r = p.kc + row_off(k0, k0 + kb * 16 + c16, blkA, blkB) * DK;
+#pragma unroll
+                for (int kk = 0; kk < KQ; ++kk) {
+                    const int dk0 = kk * 32 + grp * 8;
+                    if (dk0 < DK)
+                        kr[kb][kk] = *(const u32x4*)(r + dk0);
+                    else
+                        kr[kb][kk] = u32x4{0, 0, 0, 0};
+                }
             }
         }
     };
@@ -136,7 +162,13 @@ void decode_paged_split_kernel(SplitParams p) {
             const int off = s * 1024 + lane * 16;
             const int r = off / VROW;
             const int c = ((off % VROW) >> 4) ^ swz<NCV, true>(r);
-            load_lds16_nt(p.vc + row_off(k0, k0 + r, blkA, blkB) * DV + c * 8, vl + st * STAGE + s * 1024);
+            if constexpr (SBASE && (16 * VROW) % 1024 == 0) {
+                const char* base = kv_base(p.vc, s >= 16 * VROW / 1024 ? blkB : blkA, DV);
+                load_lds16_nt(base + (size_t)(row_in_block(k0 + r) * (DV * 2) + (uint32_t)(c * 16)),
+                              vl + st * STAGE + s * 1024);
+            } else {
+                load_lds16_nt(p.vc + row_off(k0, k0 + r, blkA, blkB) * DV + c * 8, vl + st * STAGE + s * 1024);
+            }
         }
     };
     constexpr int LOADS_PER_STEP = 2 * KQ + VSEG;  // vector-memory instructions issued per step
