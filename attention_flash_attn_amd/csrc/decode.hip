@@ -171,7 +171,6 @@ void decode_paged_split_kernel(SplitParams p) {
             }
         }
     };
-    constexpr int LOADS_PER_STEP = 2 * KQ + VSEG;  // vector-memory instructions issued per step
 
     f32x4 oacc[CB][DBV];
 #pragma unroll
@@ -186,8 +185,22 @@ void decode_paged_split_kernel(SplitParams p) {
     }
 
     // one 32-key step: S^T, online softmax, O^T += V^T P^T (K fragments in kc_, V in stage st)
-    auto compute = [&](int k0, const u32x4 (&kc_)[2][KQ], int st) {
+    // V^T fragments of stage st into registers: for column block d, rows (keys) grp*4 + 0..3 of
+    // block 0 and 16 + grp*4 + 0..3 of block 1, columns d*16 + (c16&3)*4 + 0..3
+    auto vread = [&](int st, bf16x8 (&vf)[DBV]) {
         const char* vt = vl + st * STAGE;
+        const int ra = grp * 4 + (c16 >> 2);
+        const int rb = ra + 16;
+#pragma unroll
+        for (int d = 0; d < DBV; ++d) {
+            const int dc = d * 16 + (c16 & 3) * 4;
+            const int ch = dc >> 3, within = (dc & 7) * 2;
+            const bf16x4 va = lds_read_tr16(vt + ra * VROW + ((ch ^ swz<NCV, true>(ra)) * 16) + within);
+            const bf16x4 vb = lds_read_tr16(vt + rb * VROW + ((ch ^ swz<NCV, true>(rb)) * 16) + within);
+            vf[d] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    auto compute = [&](int k0, const u32x4 (&kc_)[2][KQ], const bf16x8 (&vf)[DBV]) {
 
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
@@ -237,26 +250,10 @@ void decode_paged_split_kernel(SplitParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) l_run[cb] = add_op2<F16>(pk[j], l_run[cb]);
             const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-            // O^T += V^T P^T: V^T rows are keys grp*4 + 0..3 (block 0) and 16 + grp*4 + 0..3 (block 1)
-            const int ra = grp * 4 + (c16 >> 2);
-            const int rb = ra + 16;
+            // O^T += V^T P^T
 #pragma unroll
-            for (int d = 0; d < DBV; ++d) {
-                const int dc = d * 16 + (c16 & 3) * 4;
-                const int ch = dc >> 3, within = (dc & 7) * 2;
-                const bf16x4 va = lds_read_tr16(vt + ra * VROW + ((ch ^ swz<NCV, true>(ra)) * 16) + within);
-                const bf16x4 vb = lds_read_tr16(vt + rb * VROW + ((ch ^ swz<NCV, true>(rb)) * 16) + within);
-                oacc[cb][d] = mma16<F16>(__builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7), pb, oacc[cb][d]);
-            }
+            for (int d = 0; d < DBV; ++d) oacc[cb][d] = mma16<F16>(vf[d], pb, oacc[cb][d]);
         }
-    };
-    // wait until at most `pending` vector-memory instructions are in flight
-    auto wait_for_step = [&](bool more) {
-        if (more)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS_PER_STEP) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
     };
     auto prefetch = [&](int k0, u32x4 (&kr)[2][KQ], int st) {
         int bA, bB;
@@ -267,22 +264,31 @@ void decode_paged_split_kernel(SplitParams p) {
 
     // Two K register buffers alternate (the loop is unrolled by two so no
     // buffer is ever copied while its loads may still be in flight).
+    // Each step first waits for its own loads, reads its V^T fragments out of LDS, and only then
+    // issues the next step's loads, which run under the step's arithmetic. A transposing LDS read
+    // cannot be told apart from the direct-to-LDS copies in flight, so the compiler waits for all
+    // of them before one: reading a step's V^T while the next step's copies were in flight made
+    // every step wait for those copies before its arithmetic (64 sequences of 1024..8192 keys,
+    // 64:8 heads: d = 64 145 -> 123 us, d = 128 248 -> 244 us, d = 192 353 -> 343 us).
     u32x4 kA[2][KQ], kB[2][KQ];
+    bf16x8 vf[DBV];
     const int nsteps = (end - start + 31) / 32;
     prefetch(start, kA, 0);
     for (int it = 0; it < nsteps; it += 2) {
         const int k0 = start + it * 32;
+        wait_vmem();  // step k0's K fragments and V rows have landed
+        vread(0, vf);
         __builtin_amdgcn_sched_barrier(0);
-        const bool more1 = it + 1 < nsteps;
-        if (more1) prefetch(k0 + 32, kB, 1);
-        wait_for_step(more1);
-        compute(k0, kA, 0);
-        if (!more1) break;
+        if (it + 1 < nsteps) prefetch(k0 + 32, kB, 1);
         __builtin_amdgcn_sched_barrier(0);
-        const bool more2 = it + 2 < nsteps;
-        if (more2) prefetch(k0 + 64, kA, 0);
-        wait_for_step(more2);
-        compute(k0 + 32, kB, 1);
+        compute(k0, kA, vf);
+        if (it + 1 >= nsteps) break;
+        wait_vmem();
+        vread(1, vf);
+        __builtin_amdgcn_sched_barrier(0);
+        if (it + 2 < nsteps) prefetch(k0 + 64, kA, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(k0 + 32, kB, vf);
     }
 
 #pragma unroll
