@@ -224,6 +224,16 @@ def test_gathered_only_current_row_live():
     np.testing.assert_allclose(ro, np.broadcast_to(cur[:, None, :512], ro.shape), rtol=0, atol=1e-12)
 
 
+def test_paged_column_groups_small_dims():
+    """32-column groups (the instance that addresses K/V as block base + in-block offset) at value
+    widths whose 16-row halves fill no, one and three whole 1 KB segments (dv = 16, 32, 96), with
+    16-key blocks so every step spans two blocks, and lengths down to one key."""
+    check_paged(2, 16, 2, 16, 16, 30, 300, bs=16, Sq=4, causal=True, seed=333)
+    check_paged(2, 32, 4, 32, 32, 17, 250, bs=16, Sq=3, causal=True, softcap=20.0, seed=334)
+    check_paged(3, 24, 3, 96, 96, 1, 333, bs=128, Sq=4, sinks=True, o_dtype="bf16", seed=335)
+    check_paged(2, 16, 2, 96, 96, 1, 40, bs=16, Sq=4, causal=True, seed=336, lens=[1, 40])
+
+
 def test_paged_many_query_columns():
     """Sq * Hq / Hkv > 32 query columns per KV head (several draft tokens): column groups of 32."""
     check_paged(3, 64, 8, 128, 128, 200, 700, Sq=8, causal=True, seed=330)         # 64 columns
