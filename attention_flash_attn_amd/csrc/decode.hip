@@ -810,13 +810,17 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
         pl.split_len = Sk_max >= 16384 ? 1024 : Sk_max >= 4096 ? 512 : 256;
     } else {
         // paged: one wavefront per (split, KV head, sequence). Aim for about 4096 of them
-        // (two rounds of two waves per SIMD) with splits of 256..2048 keys: long splits
+        // (two rounds of two waves per SIMD) with splits of 256..2048 (4096) keys: long splits
         // when there are many sequences (fewer partial rows to merge), short ones when few
         const long long pairs = (long long)B * Hkv;
         const long long want = (4096 + pairs - 1) / pairs;  // splits per (KV head, sequence)
         long long len = Sk_max > 0 ? (Sk_max + want - 1) / want : 256;
+        // The fp32 partials grow with the query columns per KV head, so 32-column groups
+        // (paged_cols) take splits of up to 4096 keys (4 tokens x 8 heads, 64 sequences of
+        // up to 32K keys: 984 -> 955 us; one token stays at 2048, 8192 was slower for both)
+        const int max_sl = paged_cols(dk, Sq * (Hq / Hkv)) == 32 ? 4096 : 2048;
         int sl = 256;
-        while (sl < len && sl < 2048) sl <<= 1;
+        while (sl < len && sl < max_sl) sl <<= 1;
         pl.split_len = sl;
     }
     pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;

@@ -37,9 +37,9 @@ METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM pe
 # scaled x2, write x1 against a 1 GiB plain copy; see profiles/hbm_traffic_bench.md), valid
 # only while the kernel sources hash to the values they were measured on.
 MEASURED_TRAFFIC = {
-    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp", "../build.py"), "sha256_16": "0faed732a068c308", "bytes": 653059435},
-    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "f269e4b4c4530635", "bytes": 5035215335},
-    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "f269e4b4c4530635", "bytes": 123606788},
+    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp", "../build.py"), "sha256_16": "0faed732a068c308", "bytes": 653849049},
+    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "4ca49410d0a34b75", "bytes": 5035204832},
+    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "4ca49410d0a34b75", "bytes": 123606018},
 }
 
 

@@ -147,7 +147,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  * Decode attention: Sq query rows per sequence (Sq = 1 is the single-token
  * case) against a KV cache read in one of two modes. The keys are split into
  * fixed-size ranges processed in parallel, then merged by log-sum-exp. The
- * range length (256..2048 keys) depends only on the sizes passed here and to
+ * range length (256..4096 keys) depends only on the sizes passed here and to
  * attn_decode_workspace_bytes. Launch-size limits (ATTN_ERR_UNSUPPORTED past
  * them): B and the number of ranges at most 65535 each; B * Sq * Hq under 2^26
  * output rows; paged mode Hkv * ceil(Sq * (Hq / Hkv) / 16) under 2^26;
