@@ -117,6 +117,26 @@ def _ptr(t, name, dtype=None, allow_none=False):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dims(t, name, n):
+    """t must be an n-dimensional tensor; returns its shape."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must be a torch tensor" % name)
+    if t.dim() != n:
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must have %d dimensions (got shape %s)" % (name, n, tuple(t.shape)))
+    return tuple(int(x) for x in t.shape)
+
+
+def _expect(t, name, shape):
+    """t (if given) must have exactly this shape: the kernels read and write the sizes the
+    other tensors define, so a mismatch would run past the end of a buffer."""
+    if t is None:
+        return
+    got = tuple(int(x) for x in t.shape)
+    if got != tuple(shape):
+        raise AttnError(ATTN_ERR_INVALID_ARG, "%s must have shape %s (got %s)" % (name, tuple(shape), got))
+
+
 def _row_ptr(t, name):
     """Row array of a gathered cache: rows may be strided, each row contiguous."""
     import torch
@@ -160,15 +180,25 @@ def _kvdtype(*ts):
     return codes[ts[0].dtype]
 
 
+def _prefill_sizes(q, k, v, o, lse, sinks):
+    B, Sq, Hq, dk = _dims(q, "q", 4)
+    Bk, Sk, Hkv, dkk = _dims(k, "k", 4)
+    dv = _dims(v, "v", 4)[3]
+    _expect(k, "k", (B, Sk, Hkv, dk))
+    _expect(v, "v", (B, Sk, Hkv, dv))
+    _expect(o, "o", (B, Sq, Hq, dv))
+    _expect(lse, "lse", (B, Hq, Sq))
+    _expect(sinks, "sinks", (Hq,))
+    return B, Sq, Hq, dk, Sk, Hkv, dv
+
+
 def attn_prefill_fwd(q, k, v, o, lse=None, *, scale, causal=False, softcap=0.0, sinks=None, stream=None):
     """q [B,Sq,Hq,dk], k [B,Sk,Hkv,dk], v [B,Sk,Hkv,dv] bf16; o [B,Sq,Hq,dv] bf16|fp32;
     lse optional fp32 [B,Hq,Sq]; sinks optional fp32 [Hq]. Enqueued on `stream`
     (default: torch's current stream)."""
     import torch
     lib = load_library()
-    B, Sq, Hq, dk = q.shape
-    _, Sk, Hkv, _ = k.shape
-    dv = v.shape[3]
+    B, Sq, Hq, dk, Sk, Hkv, dv = _prefill_sizes(q, k, v, o, lse, sinks)
     st = lib.attn_prefill_fwd(_ptr(q, "q", torch.bfloat16), _ptr(k, "k", torch.bfloat16),
                               _ptr(v, "v", torch.bfloat16), _ptr(o, "o"), _odtype(o),
                               _ptr(lse, "lse", torch.float32, True),
@@ -185,9 +215,7 @@ def attn_prefill_fwd_ex(q, k, v, o, lse=None, *, scale, causal=False, softcap=0.
     ALiBi slope for max_bias."""
     import torch
     lib = load_library()
-    B, Sq, Hq, dk = q.shape
-    _, Sk, Hkv, _ = k.shape
-    dv = v.shape[3]
+    B, Sq, Hq, dk, Sk, Hkv, dv = _prefill_sizes(q, k, v, o, lse, sinks)
     mb = mh = 1
     ms = 0
     if mask is not None:
@@ -220,20 +248,40 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
     dk defaults to q's width and dv to o's. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv]."""
     import torch
     lib = load_library()
-    B, Sq, Hq, qdk = q.shape
+    B, Sq, Hq, qdk = _dims(q, "q", 4)
     paged = block_table is not None
     if paged:
-        Hkv_, bs, dk_ = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
-        dv_ = v_cache.shape[3]
+        n_blocks, Hkv_, bs, dk_ = _dims(k_cache, "k_cache", 4)
+        dv_ = _dims(v_cache, "v_cache", 4)[3]
+        _expect(v_cache, "v_cache", (n_blocks, Hkv_, bs, dv_))
         Hkv, dk, dv = Hkv_, dk_, dv_
-        max_blocks = block_table.shape[1]
+        if qdk != dk:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "q's head dim (%d) must equal the key cache's (%d)" % (qdk, dk))
+        max_blocks = _dims(block_table, "block_table", 2)[1]
+        _expect(block_table, "block_table", (B, max_blocks))
+        if seq_lens is None:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "paged mode needs seq_lens")
+        _expect(seq_lens, "seq_lens", (B,))
+        if row_index is not None or k_cur is not None or v_cur is not None:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "row_index / k_cur / v_cur belong to gathered mode")
         n_sel = 0
     else:
         bs, max_blocks = 0, 0
-        n_sel = row_index.shape[1] if row_index is not None else 0
+        if row_index is None:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "give block_table (paged mode) or row_index (gathered mode)")
+        n_sel = _dims(row_index, "row_index", 2)[1]
+        _expect(row_index, "row_index", (B, n_sel))
+        _expect(key_pos, "key_pos", (B, n_sel))
+        _expect(q_pos, "q_pos", (B,))
         Hkv = 1 if Hkv is None else Hkv
         dk = qdk if dk is None else dk
         dv = o.shape[3] if dv is None else dv
+        if qdk != dk:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "q's head dim (%d) must equal dk (%d)" % (qdk, dk))
+        if _dims(k_cache, "k_cache", 2)[1] < dk or _dims(v_cache, "v_cache", 2)[1] < dv:
+            raise AttnError(ATTN_ERR_INVALID_ARG, "k_cache rows must hold dk and v_cache rows dv elements")
+    _expect(o, "o", (B, Sq, Hq, dv))
+    _expect(sinks, "sinks", (Hq,))
     ws_bytes = workspace.numel() * workspace.element_size()
     if paged:
         kp, vp = _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
@@ -249,6 +297,8 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
             kcp, vcp = _row_ptr(k_cur, "k_cur"), _row_ptr(v_cur, "v_cur")
             if k_cur.stride(0) != kv_row_stride or v_cur.stride(0) != kv_row_stride:
                 raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur / v_cur rows must have the cache's row stride")
+            if k_cur.shape[1] < dk or v_cur.shape[1] < dv:
+                raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur rows must hold dk and v_cur rows dv elements")
             if k_cur.shape[0] < B or v_cur.shape[0] < B:
                 raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur / v_cur need one row per token")
     if paged or k_cur is None:

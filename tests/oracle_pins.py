@@ -308,6 +308,98 @@ def pin_paged(orc):
             _close(o[b], od[0], 1e-13, "paged vs dense (%s table)" % table_kind)
 
 
+def pin_paged_multi_token_causal(orc):
+    """Several query rows per sequence (a speculative draft) with the causal mask: the
+    rows are the sequence's last Sq positions, so query i of a sequence of L keys sees
+    exactly its first L - Sq + i + 1 keys (none when that is <= 0, giving o = 0). Each
+    row is checked against torch's scaled_dot_product_attention in fp64 over the
+    truncated, contiguous key set; the cache is paged through a random block table."""
+    import torch
+    rng = _rng(54)
+    B, Sq, Hq, Hkv, d, bs = 3, 4, 4, 2, 8, 4
+    lens = np.array([9, 4, 2])                  # the last sequence has fewer keys than queries
+    nblk = -(-lens // bs)
+    N = int(nblk.sum())
+    q = _rand(rng, B, Sq, Hq, d)
+    dense_k = [_rand(rng, int(L), Hkv, d) for L in lens]
+    dense_v = [_rand(rng, int(L), Hkv, d) for L in lens]
+    order = rng.permutation(N)
+    kc = _rand(rng, N, Hkv, bs, d)              # slots past a sequence's end hold noise
+    vc = _rand(rng, N, Hkv, bs, d)
+    table = np.zeros((B, 3), dtype=np.int32)
+    p = 0
+    for b, L in enumerate(lens):
+        for j in range(int(nblk[b])):
+            phys = order[p]
+            p += 1
+            table[b, j] = phys
+            n = min(bs, int(L) - j * bs)
+            kc[phys, :, :n] = dense_k[b][j * bs:j * bs + n].transpose(1, 0, 2)
+            vc[phys, :, :n] = dense_v[b][j * bs:j * bs + n].transpose(1, 0, 2)
+    o, lse = orc.decode_paged(q, kc, vc, table, lens, 0.35, causal=True)
+    for b, L in enumerate(lens):
+        for i in range(Sq):
+            n_vis = int(L) - Sq + i + 1
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                if n_vis <= 0:
+                    _close(o[b, i, h], np.zeros(d), 0.0, "draft row with no visible key")
+                    assert lse[b, h, i] == -np.inf, "lse of a draft row with no visible key"
+                    continue
+                qt = torch.from_numpy(q[b, i, h][None, None, None, :])
+                kt = torch.from_numpy(np.ascontiguousarray(dense_k[b][:n_vis, g])[None, None])
+                vt = torch.from_numpy(np.ascontiguousarray(dense_v[b][:n_vis, g])[None, None])
+                ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.35)
+                _close(o[b, i, h], ref[0, 0, 0].numpy(), 1e-13,
+                       "draft row %d of sequence %d (%d visible keys)" % (i, b, n_vis))
+
+
+def pin_bf16_bit_patterns(orc):
+    """Inputs given as bf16 bit patterns (uint16) are widened exactly: hand-worked
+    patterns (bf16 is sign, 8 exponent bits with bias 127, 7 fraction bits; the
+    all-zero exponent holds subnormals fraction/128 * 2^-126), torch's own
+    bfloat16 -> float64 conversion on random bit patterns, and the attention entry
+    points giving the same result on bit patterns as on the widened values."""
+    import torch
+    table = {
+        0x3F80: 1.0, 0xC040: -3.0, 0x3E80: 0.25, 0xBF00: -0.5, 0x4049: 3.140625,
+        0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x007F: 127 * 2.0 ** -133, 0x8001: -(2.0 ** -133),
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x7F80: np.inf, 0xFF80: -np.inf,
+    }
+    bits = np.array(list(table), dtype=np.uint16)
+    got = orc.bf16_bits_to_f64(bits)
+    assert got.dtype == np.float64
+    for b, want in zip(bits, got):
+        assert want == table[int(b)], "bf16 0x%04X widened to %r, expected %r" % (b, want, table[int(b)])
+    z = orc.bf16_bits_to_f64(np.array([0x0000, 0x8000], dtype=np.uint16))
+    assert z[0] == 0.0 and z[1] == 0.0 and not np.signbit(z[0]) and np.signbit(z[1]), "signed zeros"
+    rb = _rng(81).integers(0, 1 << 16, 4096).astype(np.uint16)
+    rb = rb[(rb & 0x7F80) != 0x7F80]            # finite patterns (no inf / NaN)
+    ref = torch.from_numpy(rb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(orc.bf16_bits_to_f64(rb), ref), "widening differs from torch's bfloat16 conversion"
+
+    def bits_and_values(shape, seed):
+        x = torch.from_numpy(_rand(_rng(seed), *shape)).to(torch.bfloat16)
+        return x.view(torch.int16).numpy().view(np.uint16), x.to(torch.float64).numpy()
+    qb, qf = bits_and_values((1, 5, 2, 8), 82)
+    kb, kf = bits_and_values((1, 6, 1, 8), 83)
+    vb, vf = bits_and_values((1, 6, 1, 8), 84)
+    o1, l1 = orc.prefill(qb, kb, vb, 0.3, causal=True)
+    o2, l2 = orc.prefill(qf, kf, vf, 0.3, causal=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "prefill on bit patterns vs values"
+    kcb, kcf = bits_and_values((3, 1, 4, 8), 85)
+    vcb, vcf = bits_and_values((3, 1, 4, 8), 86)
+    tab = np.array([[2, 0, 1]], dtype=np.int32)
+    o1, _ = orc.decode_paged(qb[:, :1], kcb, vcb, tab, np.array([10]), 0.3)
+    o2, _ = orc.decode_paged(qf[:, :1], kcf, vcf, tab, np.array([10]), 0.3)
+    assert np.array_equal(o1, o2), "paged decode on bit patterns vs values"
+    rowb, rowf = bits_and_values((7, 8), 87)
+    ri = np.array([[4, 0, 6]], dtype=np.int32)
+    o1, _ = orc.decode_gathered(qb[0, :1], rowb, rowb[:, :5], ri, np.array([[1.0, 2.0, 3.0]]), np.array([2]), 0.3)
+    o2, _ = orc.decode_gathered(qf[0, :1], rowf, rowf[:, :5], ri, np.array([[1.0, 2.0, 3.0]]), np.array([2]), 0.3)
+    assert np.array_equal(o1, o2), "gathered decode on bit patterns vs values"
+
+
 def pin_gathered(orc):
     """Gathered decode equals dense attention over the selected rows that lie at or
     before the token (a key exactly at the token's position counts), ignores the

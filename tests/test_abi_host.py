@@ -216,3 +216,98 @@ def test_mla_tail_workspace_bytes():
     assert n >= 16 * 128 * 128 * 2 + 16 * 7168 * 4
     assert (n - 16 * 128 * 128 * 2) % (16 * 7168 * 4) == 0
     assert attn.attn_mla_tail_workspace_bytes(0, 128, 512, 128, 7168) == 0
+
+
+# ---------------------------------------------------------------- binding shape checks
+# The binding derives every size from q, k and v (or the caches) and checks each other
+# tensor against them before any pointer is taken, so these run on CPU tensors: a shape
+# mismatch raises INVALID_ARG naming the tensor (a correct shape only fails later, at the
+# "must be on the GPU" check).
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def _raises_shape(fn, name):
+    with pytest.raises(binding.AttnError) as ei:
+        fn()
+    assert ei.value.status == binding.ATTN_ERR_INVALID_ARG
+    assert name in str(ei.value) and "GPU" not in str(ei.value), str(ei.value)
+
+
+def _prefill_args(**kw):
+    import torch
+    a = dict(q=_t(2, 8, 4, 64), k=_t(2, 8, 2, 64), v=_t(2, 8, 2, 64), o=_t(2, 8, 4, 64), lse=None, sinks=None)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("o", dict(o=_t(2, 8, 4, 32))),
+    ("o", dict(o=_t(1, 8, 4, 64))),
+    ("k", dict(k=_t(2, 8, 2, 32))),
+    ("k", dict(k=_t(1, 8, 2, 64))),
+    ("v", dict(v=_t(2, 7, 2, 64))),
+    ("lse", dict(lse=_t(2, 4, 9, dtype=None))),
+    ("sinks", dict(sinks=_t(3))),
+    ("q", dict(q=_t(2, 8, 64))),
+])
+def test_binding_prefill_rejects_mismatched_shapes(name, bad):
+    a = _prefill_args(**bad)
+    _raises_shape(lambda: binding.attn_prefill_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], scale=0.1,
+                                                   sinks=a["sinks"]), name)
+    _raises_shape(lambda: binding.attn_prefill_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], scale=0.1,
+                                                      sinks=a["sinks"]), name)
+
+
+def test_binding_prefill_good_shapes_reach_the_device_check():
+    a = _prefill_args()
+    with pytest.raises(binding.AttnError) as ei:
+        binding.attn_prefill_fwd(a["q"], a["k"], a["v"], a["o"], None, scale=0.1)
+    assert "GPU" in str(ei.value)
+
+
+def _paged_args(**kw):
+    import torch
+    a = dict(q=_t(3, 1, 8, 64), kc=_t(10, 2, 16, 64), vc=_t(10, 2, 16, 64), o=_t(3, 1, 8, 64),
+             table=_t(3, 4, dtype=torch.int32), lens=_t(3, dtype=torch.int32), sinks=None)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("q's head dim", dict(q=_t(3, 1, 8, 32))),
+    ("o", dict(o=_t(3, 1, 8, 32))),
+    ("o", dict(o=_t(3, 2, 8, 64))),
+    ("v_cache", dict(vc=_t(10, 1, 16, 64))),
+    ("block_table", dict(table=_t(2, 4))),
+    ("seq_lens", dict(lens=_t(4))),
+    ("sinks", dict(sinks=_t(4))),
+])
+def test_binding_paged_rejects_mismatched_shapes(name, bad):
+    a = _paged_args(**bad)
+    _raises_shape(lambda: binding.attn_decode_fwd(a["q"], a["kc"], a["vc"], a["o"], _t(16), scale=0.1, Sk_max=64,
+                                                  block_table=a["table"], seq_lens=a["lens"], sinks=a["sinks"]),
+                  name)
+
+
+def _gathered_args(**kw):
+    import torch
+    a = dict(q=_t(2, 1, 16, 576), rows=_t(100, 576), o=_t(2, 1, 16, 512), ri=_t(2, 5, dtype=torch.int32),
+             kp=_t(2, 5, dtype=torch.float32), qp=_t(2, dtype=torch.int32))
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("o", dict(o=_t(2, 1, 16, 256))),
+    ("key_pos", dict(kp=_t(2, 4))),
+    ("q_pos", dict(qp=_t(3))),
+    ("row_index", dict(ri=_t(2, 5, 1))),
+    ("q's head dim", dict(q=_t(2, 1, 16, 512))),
+])
+def test_binding_gathered_rejects_mismatched_shapes(name, bad):
+    a = _gathered_args(**bad)
+    _raises_shape(lambda: binding.attn_decode_fwd(a["q"], a["rows"], a["rows"][:, :512], a["o"], _t(16), scale=0.1,
+                                                  Sk_max=5, row_index=a["ri"], key_pos=a["kp"], q_pos=a["qp"],
+                                                  dk=576, dv=512), name)

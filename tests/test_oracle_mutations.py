@@ -1,7 +1,8 @@
 """Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
 the pin set catches every one of them. This shows the pins constrain each part
 of the definition: the scale, the softcap, the sink term, the causal alignment,
-the GQA head map, the value operand, the lse, the paged and gathered indexing."""
+the GQA head map, the value operand, the lse, the paged and gathered indexing,
+the draft rows' causal offset in paged decode and the widening of bf16 bit patterns."""
 
 import importlib.util
 import os
@@ -48,6 +49,9 @@ MUTATIONS = {
     "tail_absorb_layout_r_major": ("u[:, h, :] = o[:, h, :] @ wa[h].T", "u[:, h, :] = o[:, h, :] @ wa[h].reshape(R, DV)"),
     "tail_absorb_wrong_head": ("u[:, h, :] = o[:, h, :] @ wa[h].T", "u[:, h, :] = o[:, h, :] @ wa[(h + 1) % H].T"),
     "tail_concat_value_major": ("y = u.reshape(T, H * DV) @ wo", "y = u.transpose(0, 2, 1).reshape(T, H * DV) @ wo"),
+    "bf16_widen_shift_15": ("(b.astype(np.uint32) << 16)", "(b.astype(np.uint32) << 15)"),
+    "paged_draft_offset_plus_one": ("np.arange(Sq) + (L - Sq)", "np.arange(Sq) + (L - Sq + 1)"),
+    "paged_draft_all_at_last_key": ("np.arange(Sq) + (L - Sq)", "np.full(Sq, L - 1)"),
 }
 
 
