@@ -88,17 +88,56 @@ def test_paged_block_permutation_invariance():
     assert torch.equal(o1, o2)
 
 
-def test_config4_full_size_sampled():
+def test_config4_full_size():
+    """Every output element of the paged decode workload (64 sequences of up to 32768 keys)."""
     c = synth.CONFIGS["c4_paged_gqa_decode"]
-    print("full-size c4 paged decode", flush=True)
+    print("full-size c4 paged decode, every element", flush=True)
     case = synth.paged_case(c["seed"], c["B"], c["Hq"], c["Hkv"], c["dk"], c["dv"], c["len_lo"], c["len_hi"],
                             block_size=c["block_size"])
     o = run_paged(case, c["scale"], False, 0.0, "bf16", c["len_hi"])
-    batches = [0, 1, int(np.argmax(case["seq_lens"])), int(np.argmin(case["seq_lens"])), 63]
     ro, _ = oracle.decode_paged(case["q"], case["k_cache"], case["v_cache"], case["block_table"],
-                                case["seq_lens"], c["scale"], batches=batches)
-    err, cos = check_close(host(o)[batches], ro, "bf16", "config 4")
-    print("config 4 sampled: max err %.3g cos %.8f" % (err, cos))
+                                case["seq_lens"], c["scale"])
+    err, cos = check_close(host(o), ro, "bf16", "config 4")
+    print("config 4, %d elements: max err %.3g cos %.8f" % (ro.size, err, cos))
+
+
+def _planned_split(B, Hq, Hkv, Sq, Sk_max, dk, dv):
+    """Key-split length the library plans, read back from the workspace size
+    (rows * n_split * (dv + 2) fp32, rounded up to 256 bytes)."""
+    ws = binding.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk_max, dk, dv)
+    rows = B * Sq * Hq
+    n_split = ws // (rows * (dv + 2) * 4)
+    for sl in (256, 512, 1024, 2048, 4096):
+        if -(-Sk_max // sl) == n_split:
+            return sl
+    raise AssertionError("no split length matches a workspace of %d bytes" % ws)
+
+
+def test_paged_split_lengths_512_1024():
+    """Shapes whose (sequence, KV head) count plans 512- and 1024-key splits."""
+    assert _planned_split(8, 16, 8, 1, 20000, 128, 128) == 512
+    check_paged(8, 16, 8, 128, 128, 9000, 20000, seed=210)
+    assert _planned_split(16, 8, 8, 1, 20000, 64, 64) == 1024
+    check_paged(16, 8, 8, 64, 64, 12000, 20000, causal=True, Sq=1, o_dtype="bf16", seed=211)
+    assert _planned_split(16, 64, 8, 2, 20000, 64, 64) == 1024      # 16 columns per KV head
+    check_paged(16, 64, 8, 64, 64, 15000, 20000, Sq=2, causal=True, seed=212)
+
+
+def test_config4_shape_draft_tokens_4096_key_splits():
+    """The workload's shape with 4 causal draft tokens per sequence: 32 query columns per KV
+    head take the 32-column instance and 4096-key splits. Sequences of the longest,
+    shortest and a few other lengths are compared with the oracle."""
+    c = synth.CONFIGS["c4_paged_gqa_decode"]
+    assert _planned_split(c["B"], c["Hq"], c["Hkv"], 4, c["len_hi"], c["dk"], c["dv"]) == 4096
+    print("config 4 shape, 4 draft tokens, causal", flush=True)
+    case = synth.paged_case(c["seed"], c["B"], c["Hq"], c["Hkv"], c["dk"], c["dv"], c["len_lo"], c["len_hi"],
+                            block_size=c["block_size"], Sq=4)
+    o = run_paged(case, c["scale"], True, 0.0, "bf16", c["len_hi"])
+    batches = [0, 1, int(np.argmax(case["seq_lens"])), int(np.argmin(case["seq_lens"])), 40, 63]
+    ro, _ = oracle.decode_paged(case["q"], case["k_cache"], case["v_cache"], case["block_table"],
+                                case["seq_lens"], c["scale"], causal=True, batches=batches)
+    err, cos = check_close(host(o)[batches], ro, "bf16", "config 4 shape, 4 draft tokens")
+    print("4 draft tokens: max err %.3g cos %.8f" % (err, cos))
 
 
 # ---------------------------------------------------------------- gathered rows (MLA-style)
@@ -170,6 +209,19 @@ def test_config5_full_size():
     print("full-size c5 gathered decode", flush=True)
     o, ro = check_gathered(c["T"], c["Hq"], c["n_rows"], c["n_sel"], o_dtype="bf16", seed=c["seed"])
     print("config 5: max err %.3g" % np.abs(o - ro).max())
+
+
+def test_gathered_bitwise_repeatable():
+    """Two launches of the gathered decode on the same inputs give identical bits (the
+    split partials are merged in a fixed order)."""
+    c = synth.CONFIGS["c5_gathered_mla_decode"]
+    print("gathered decode repeatability at the workload shape", flush=True)
+    case = synth.gathered_case(c["seed"], c["T"], c["Hq"], c["dk"], c["dv"], c["n_rows"], c["n_sel"],
+                               row_dim=c["row_dim"], future_keys=64)
+    outs = [run_gathered(case, c["Hq"], c["dk"], c["dv"], c["scale"], o_dtype=od) for od in ("bf16", "bf16", "f32",
+                                                                                          "f32")]
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(outs[2].view(torch.int32), outs[3].view(torch.int32))
 
 
 def test_gathered_current_row():
