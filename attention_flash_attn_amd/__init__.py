@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     attn_prefill_fwd,
     attn_prefill_fwd_ex,
     attn_decode_fwd,
+    attn_decode_fwd_noalloc,
     attn_decode_workspace_bytes,
     attn_dequant_fp16,
     attn_mla_tail,

@@ -76,6 +76,8 @@ def load_library():
                                         c_void_p, c_int, c_int, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_int, ctypes.c_int64,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        lib.attn_decode_fwd_noalloc.restype = c_int
+        lib.attn_decode_fwd_noalloc.argtypes = lib.attn_decode_fwd.argtypes[:-3] + [c_void_p]
         lib.attn_mla_tail_workspace_bytes.restype = c_size_t
         lib.attn_mla_tail_workspace_bytes.argtypes = [c_int] * 5
         lib.attn_mla_tail.restype = c_int
@@ -245,9 +247,32 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
     views [rows, width] sharing one row stride (e.g. kv[:, :dk] and kv[:, 64:]), with
     row_index [B,n_sel] int32, key_pos [B,n_sel] fp32, q_pos [B] int32, and optionally the
     tokens' own rows k_cur / v_cur as 2-D row views [B, width] with the same row stride;
-    dk defaults to q's width and dv to o's. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv]."""
-    import torch
+    dk defaults to q's width and dv to o's. q [B,Sq,Hq,dk] bf16, o [B,Sq,Hq,dv].
+    workspace: a GPU tensor of at least attn_decode_workspace_bytes(...) bytes."""
     lib = load_library()
+    args = _decode_args(q, k_cache, v_cache, o, scale, Sk_max, causal, softcap, sinks, block_table, seq_lens,
+                        row_index, key_pos, q_pos, kv_row_stride, Hkv, dk, dv, k_cur, v_cur)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode_fwd(*args, _ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
+
+
+def attn_decode_fwd_noalloc(q, k_cache, v_cache, o, *, scale, Sk_max, causal=False, softcap=0.0,
+                            sinks=None, block_table=None, seq_lens=None, row_index=None, key_pos=None,
+                            q_pos=None, kv_row_stride=0, Hkv=None, dk=None, dv=None, k_cur=None, v_cur=None,
+                            stream=None):
+    """attn_decode_fwd without a workspace: the split-KV partials go to the library's static
+    per-GPU scratch (at most ATTN_NOALLOC_SCRATCH_BYTES; larger sizes raise ATTN_ERR_UNSUPPORTED).
+    Calls that overlap on one GPU race; calls ordered on one stream are safe."""
+    lib = load_library()
+    args = _decode_args(q, k_cache, v_cache, o, scale, Sk_max, causal, softcap, sinks, block_table, seq_lens,
+                        row_index, key_pos, q_pos, kv_row_stride, Hkv, dk, dv, k_cur, v_cur)
+    _check(lib.attn_decode_fwd_noalloc(*args, _stream(stream)))
+
+
+def _decode_args(q, k_cache, v_cache, o, scale, Sk_max, causal, softcap, sinks, block_table, seq_lens,
+                 row_index, key_pos, q_pos, kv_row_stride, Hkv, dk, dv, k_cur, v_cur):
+    """Checked C arguments of a decode call, up to (not including) the workspace."""
+    import torch
     B, Sq, Hq, qdk = _dims(q, "q", 4)
     paged = block_table is not None
     if paged:
@@ -282,7 +307,6 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
             raise AttnError(ATTN_ERR_INVALID_ARG, "k_cache rows must hold dk and v_cache rows dv elements")
     _expect(o, "o", (B, Sq, Hq, dv))
     _expect(sinks, "sinks", (Hq,))
-    ws_bytes = workspace.numel() * workspace.element_size()
     if paged:
         kp, vp = _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache")
     else:
@@ -303,16 +327,15 @@ def attn_decode_fwd(q, k_cache, v_cache, o, workspace, *, scale, Sk_max, causal=
                 raise AttnError(ATTN_ERR_INVALID_ARG, "k_cur / v_cur need one row per token")
     if paged or k_cur is None:
         kcp, vcp = None, None
-    st = lib.attn_decode_fwd(_ptr(q, "q"), kp, vp, _ptr(o, "o"), _odtype(o), _qdtype(q), _kvdtype(k_cache, v_cache),
-                             B, Hq, Hkv, Sq, int(Sk_max), dk, dv, float(scale), int(bool(causal)),
-                             float(softcap), _ptr(sinks, "sinks", torch.float32, True),
-                             _ptr(block_table, "block_table", torch.int32, True), bs, max_blocks,
-                             _ptr(seq_lens, "seq_lens", torch.int32, True),
-                             _ptr(row_index, "row_index", torch.int32, True),
-                             _ptr(key_pos, "key_pos", torch.float32, True),
-                             _ptr(q_pos, "q_pos", torch.int32, True), n_sel, int(kv_row_stride),
-                             kcp, vcp, _ptr(workspace, "workspace"), ws_bytes, _stream(stream))
-    _check(st)
+    return (_ptr(q, "q"), kp, vp, _ptr(o, "o"), _odtype(o), _qdtype(q), _kvdtype(k_cache, v_cache),
+            B, Hq, Hkv, Sq, int(Sk_max), dk, dv, float(scale), int(bool(causal)),
+            float(softcap), _ptr(sinks, "sinks", torch.float32, True),
+            _ptr(block_table, "block_table", torch.int32, True), bs, max_blocks,
+            _ptr(seq_lens, "seq_lens", torch.int32, True),
+            _ptr(row_index, "row_index", torch.int32, True),
+            _ptr(key_pos, "key_pos", torch.float32, True),
+            _ptr(q_pos, "q_pos", torch.int32, True), n_sel, int(kv_row_stride),
+            kcp, vcp)
 
 
 def attn_dequant_fp16(src, fmt, dst, stream=None):

@@ -10,6 +10,8 @@
 
 #include "attn_launch.hpp"
 
+static_assert(attn::kNoallocScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES, "scratch size of the header and the library");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -167,14 +169,16 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
     return decode_too_large(B, pl) ? 0 : pl.ws_bytes;
 }
 
-attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype,
-                            int q_dtype, int kv_dtype, int B,
-                            int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv, float scale, int causal,
-                            float softcap, const float* sinks, const int32_t* block_table, int block_size,
-                            int max_blocks_per_seq, const int32_t* seq_lens, const int32_t* row_index,
-                            const float* key_pos, const int32_t* q_pos, int n_sel, int64_t kv_row_stride,
-                            const void* k_cur, const void* v_cur, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+// Checks and launches a decode call. noalloc: the split-KV workspace is the library's static
+// device scratch (workspace / workspace_bytes are ignored) instead of the caller's buffer.
+static attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype,
+                               int q_dtype, int kv_dtype, int B,
+                               int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv, float scale, int causal,
+                               float softcap, const float* sinks, const int32_t* block_table, int block_size,
+                               int max_blocks_per_seq, const int32_t* seq_lens, const int32_t* row_index,
+                               const float* key_pos, const int32_t* q_pos, int n_sel, int64_t kv_row_stride,
+                               const void* k_cur, const void* v_cur, void* workspace, size_t workspace_bytes,
+                               bool noalloc, void* stream) {
     if (!q || !k_cache || !v_cache || !o) return fail(ATTN_ERR_INVALID_ARG, "q, k_cache, v_cache and o are required");
     attn_status st = check_common(B, Hq, Hkv, Sq, dk, dv, scale, softcap, o_dtype);
     if (st != ATTN_OK) return st;
@@ -222,9 +226,21 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
         return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large: Hkv * Sq * (Hq / Hkv) / 16 must be under 2^26");
     if (gathered && (Hq + 63) / 64 > 65535)
         return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large: gathered mode takes at most 65535 * 64 heads");
-    if (!workspace || workspace_bytes < pl.ws_bytes)
-        return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", pl.ws_bytes, workspace_bytes);
-    if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (noalloc) {
+        if (pl.ws_bytes > attn::kNoallocScratchBytes)
+            return fail(ATTN_ERR_UNSUPPORTED,
+                        "attn_decode_fwd_noalloc: these sizes need %zu bytes of split-KV scratch, more than the "
+                        "%zu-byte static scratch; use attn_decode_fwd with a workspace",
+                        pl.ws_bytes, attn::kNoallocScratchBytes);
+        // all argument checks are done: the first HIP call is the scratch lookup
+        hipError_t e = attn::noalloc_scratch((hipStream_t)stream, &workspace);
+        if (e != hipSuccess)
+            return fail(ATTN_ERR_HIP, "no-allocation scratch lookup failed: %s", hipGetErrorString(e));
+    } else {
+        if (!workspace || workspace_bytes < pl.ws_bytes)
+            return fail(ATTN_ERR_INVALID_ARG, "workspace of %zu bytes needed (got %zu)", pl.ws_bytes, workspace_bytes);
+        if (!aligned16(workspace)) return fail(ATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    }
 
     attn::DecodeArgs a;
     a.q = q;
@@ -260,6 +276,31 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
     hipError_t e = attn::launch_decode(a, pl, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype,
+                            int q_dtype, int kv_dtype, int B,
+                            int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv, float scale, int causal,
+                            float softcap, const float* sinks, const int32_t* block_table, int block_size,
+                            int max_blocks_per_seq, const int32_t* seq_lens, const int32_t* row_index,
+                            const float* key_pos, const int32_t* q_pos, int n_sel, int64_t kv_row_stride,
+                            const void* k_cur, const void* v_cur, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    return decode_impl(q, k_cache, v_cache, o, o_dtype, q_dtype, kv_dtype, B, Hq, Hkv, Sq, Sk_max, dk, dv, scale,
+                       causal, softcap, sinks, block_table, block_size, max_blocks_per_seq, seq_lens, row_index,
+                       key_pos, q_pos, n_sel, kv_row_stride, k_cur, v_cur, workspace, workspace_bytes, false, stream);
+}
+
+attn_status attn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, int o_dtype,
+                                    int q_dtype, int kv_dtype, int B,
+                                    int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv, float scale, int causal,
+                                    float softcap, const float* sinks, const int32_t* block_table, int block_size,
+                                    int max_blocks_per_seq, const int32_t* seq_lens, const int32_t* row_index,
+                                    const float* key_pos, const int32_t* q_pos, int n_sel, int64_t kv_row_stride,
+                                    const void* k_cur, const void* v_cur, void* stream) {
+    return decode_impl(q, k_cache, v_cache, o, o_dtype, q_dtype, kv_dtype, B, Hq, Hkv, Sq, Sk_max, dk, dv, scale,
+                       causal, softcap, sinks, block_table, block_size, max_blocks_per_seq, seq_lens, row_index,
+                       key_pos, q_pos, n_sel, kv_row_stride, k_cur, v_cur, nullptr, 0, true, stream);
 }
 
 attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blocks, void* stream) {

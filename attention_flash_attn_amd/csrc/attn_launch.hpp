@@ -71,6 +71,12 @@ struct DecodePlan {
     size_t ws_bytes; // partial O (fp32, dv per row per split) + (max, sum) per row per split
 };
 
+// Size of the static device scratch that attn_decode_fwd_noalloc uses as its workspace.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+// Device address of that scratch on the device that runs `stream` (looked up once per
+// device with hipGetSymbolAddress, then cached).
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 bool decode_supported(int dk, int dv, bool gathered);
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);

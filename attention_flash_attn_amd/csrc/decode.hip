@@ -17,8 +17,15 @@
 // prefill kernel (one query per lane column); K fragments are loaded straight
 // from HBM into MFMA operand registers (16-byte vectors, whole rows consumed by
 // one wave), V goes through a small LDS block for the transposing read.
+#include <mutex>
+
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
+
+// Split-KV scratch of the no-allocation decode entry point: one copy per GPU, held for the
+// life of the process. In host code this name is only a stand-in for the symbol: kernels
+// and copies take the device address that noalloc_scratch() looks up, never this name.
+static __device__ __align__(256) char scratch[attn::kNoallocScratchBytes];
 
 namespace attn {
 namespace {
@@ -828,6 +835,39 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
     pl.ws_bytes = (size_t)pl.n_rows * pl.n_split * ((size_t)dv + 2) * sizeof(float);
     pl.ws_bytes = (pl.ws_bytes + 255) & ~(size_t)255;
     return pl;
+}
+
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr) {
+    // the device that runs work queued on `stream` (the current device for the null stream)
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // each GPU holds its own copy of the array at its own address: look it up once per
+        // device, with that device current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {

@@ -36,7 +36,8 @@
  *   - All argument checks run before any HIP call. On an error status nothing
  *     has been enqueued and the outputs are untouched (ATTN_ERR_HIP: a launch
  *     failed; outputs are then undefined). attn_last_error() gives a message.
- *   - Thread-safe; the library holds no state across calls.
+ *   - Thread-safe; the library holds no state across calls, apart from the
+ *     per-GPU scratch of attn_decode_fwd_noalloc (see there).
  *   - GQA: query head h reads KV head h / (Hq / Hkv) (contiguous groups);
  *     Hq must be a multiple of Hkv.
  *   - Causal masking is bottom-right aligned: query i of a sequence with Sq
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum attn_status {
     ATTN_OK = 0,
@@ -198,6 +199,33 @@ attn_status attn_decode_fwd(const void* q, const void* k_cache, const void* v_ca
                             const void* k_cur, const void* v_cur,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Decode without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, modes, results and errors are those of attn_decode_fwd; the split-KV partial
+ * results go to a static device array of the library (ATTN_NOALLOC_SCRATCH_BYTES per GPU,
+ * held until the process ends) instead of a caller-owned workspace. The call allocates
+ * nothing: its first call on a GPU looks up that GPU's copy of the array (the GPU that runs
+ * `stream`) and caches the address.
+ *   - Sizes whose workspace (attn_decode_workspace_bytes) exceeds ATTN_NOALLOC_SCRATCH_BYTES
+ *     return ATTN_ERR_UNSUPPORTED; use attn_decode_fwd with a workspace for them.
+ *   - Every call on one GPU shares that GPU's array: two calls whose execution overlaps on
+ *     one GPU (different streams, or host threads enqueueing concurrently on different
+ *     streams) race and give undefined results. Calls ordered on one stream are safe.
+ *   - The array keeps the last call's contents; no call relies on them.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+attn_status attn_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    void* o, int o_dtype, int q_dtype, int kv_dtype,
+                                    int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv,
+                                    float scale, int causal, float softcap, const float* sinks,
+                                    const int32_t* block_table, int block_size, int max_blocks_per_seq,
+                                    const int32_t* seq_lens,
+                                    const int32_t* row_index, const float* key_pos, const int32_t* q_pos,
+                                    int n_sel, int64_t kv_row_stride,
+                                    const void* k_cur, const void* v_cur,
+                                    void* stream);
 
 /*
  * Block formats of a quantized KV cache (32 values per block, IEEE fp16

@@ -311,3 +311,21 @@ def test_binding_gathered_rejects_mismatched_shapes(name, bad):
     _raises_shape(lambda: binding.attn_decode_fwd(a["q"], a["rows"], a["rows"][:, :512], a["o"], _t(16), scale=0.1,
                                                   Sk_max=5, row_index=a["ri"], key_pos=a["kp"], q_pos=a["qp"],
                                                   dk=576, dv=512), name)
+
+
+def test_noalloc_rejects_sizes_past_the_static_scratch():
+    """attn_decode_fwd_noalloc refuses sizes whose split-KV partials exceed the static
+    scratch (before any HIP call) and accepts the same checks as attn_decode_fwd."""
+    lib = binding.load_library()
+    i32 = ctypes.c_int
+
+    def call(B, Hq, Sq, Sk_max):
+        return lib.attn_decode_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, 0, 0, 0, B, Hq, 8, Sq, Sk_max, 128, 128,
+                                           ctypes.c_float(0.1), 0, ctypes.c_float(0.0), None, FAKE, 64, 512,
+                                           FAKE, None, None, None, 0, ctypes.c_int64(0), None, None, None)
+    # 64 sequences x 64 heads x 4 draft tokens of up to 32K keys need 68 MB of partials
+    assert binding.attn_decode_workspace_bytes(64, 64, 8, 4, 32768, 128, 128) > (64 << 20)
+    assert call(64, 64, 4, 32768) == binding.ATTN_ERR_UNSUPPORTED
+    assert b"static scratch" in lib.attn_last_error()
+    # the ordinary argument checks come first
+    assert call(0, 64, 1, 32768) == binding.ATTN_ERR_INVALID_ARG
