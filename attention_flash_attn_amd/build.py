@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libattn.so")
-SOURCES = ["prefill.hip", "prefill_d256.hip", "decode.hip", "dequant.hip", "mla_tail.hip", "abi.cpp"]
+SOURCES = ["prefill.hip", "prefill_d256.hip", "decode.hip", "decode_gathered.hip", "dequant.hip", "mla_tail.hip",
+           "abi.cpp"]
 # per-source compiler options: the head-dim-256 prefill kernels and the MLA tail use
 # the max-ILP machine scheduler (measured 3% and 2% faster; 4% slower for head dim 128).
 # The decode kernels keep MFMA accumulators in ordinary VGPRs: with them in AGPRs the

@@ -224,8 +224,10 @@ static attn_status decode_impl(const void* q, const void* k_cache, const void* v
     // the gathered kernel's second one the 64-head groups
     if (paged && (int64_t)Hkv * (((int64_t)Sq * (Hq / Hkv) + 15) / 16) > (int64_t(1) << 26) - 1)
         return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large: Hkv * Sq * (Hq / Hkv) / 16 must be under 2^26");
-    if (gathered && (Hq + 63) / 64 > 65535)
-        return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large: gathered mode takes at most 65535 * 64 heads");
+    // the gathered split pass runs one workgroup per (token, 64 query heads, key range) in a
+    // 1-D grid
+    if (gathered && (long long)B * attn::gathered_head_groups(Hq) * pl.n_split > 0x7fffffffLL)
+        return fail(ATTN_ERR_UNSUPPORTED, "decode grid too large: B * ceil(Hq / 64) * key ranges must be under 2^31");
     if (noalloc) {
         if (pl.ws_bytes > attn::kNoallocScratchBytes)
             return fail(ATTN_ERR_UNSUPPORTED,

@@ -192,6 +192,13 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
         (ATTN_LDS bf16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
 
+// The same read through an LDS-typed pointer. With the pointer's provenance kept (no
+// integer round trip) the compiler can tell the read from direct-to-LDS copies into other
+// LDS objects, instead of waiting for every copy in flight before it.
+__device__ __forceinline__ bf16x4 lds_read_tr16_l(const ATTN_LDS char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ATTN_LDS bf16x4*)p);
+}
+
 // 16-byte chunk swizzle of LDS rows holding NCH chunks. The LDS serves 256
 // bytes per cycle (64 banks of 4 bytes); a row's logical chunk c is stored at
 // c ^ swz(r) so that the reads each kernel issues are conflict-free:

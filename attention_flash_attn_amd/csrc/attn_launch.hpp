@@ -68,7 +68,7 @@ struct DecodePlan {
     int split_len;   // keys per split (multiple of the kernel's key tile)
     int n_split;     // ceil(Sk_max / split_len)
     int64_t n_rows;  // B * Sq * Hq output rows
-    size_t ws_bytes; // partial O (fp32, dv per row per split) + (max, sum) per row per split
+    size_t ws_bytes; // partial O (fp32 or bf16, dv per row per split) + (max, sum) per row per split
 };
 
 // Size of the static device scratch that attn_decode_fwd_noalloc uses as its workspace.
@@ -78,8 +78,16 @@ constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 
 bool decode_supported(int dk, int dv, bool gathered);
+// Gathered mode: rows per key range the LDS index table holds (a range of up to 1024
+// selected keys plus the token's own row, rounded up to whole 32-key steps); query heads
+// per workgroup are grouped by 64.
+constexpr int kGatherMaxSplit = 1024 + 32;
+int gathered_head_groups(int Hq);
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+// Gathered mode's split pass (decode_gathered.hip): bf16 O_s / l_s rows into ws_o, (max, sum) into ws_ml.
+hipError_t launch_gathered_split(const DecodeArgs& a, const DecodePlan& plan, uint16_t* ws_o, float* ws_ml,
+                                 hipStream_t stream);
 
 // Block dequantization to fp16: fmt 0 = q8_0 (34-byte blocks), 1 = q4_0 (18-byte blocks).
 hipError_t launch_dequant(const void* src, int fmt, void* dst, long long n_blocks, hipStream_t stream);

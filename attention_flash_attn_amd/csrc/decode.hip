@@ -318,317 +318,8 @@ void decode_paged_split_kernel(SplitParams p) {
     }
 }
 
-// Gathered mode: one workgroup per (key split, group of NW*16 heads, token).
-// The selected rows of the token are gathered straight from the row cache in
-// their native layout (the approach of the "MLA Decode Attention Kernel API
-// Reference" page, Background: no pre-gathered copy), 32 rows per step, into
-// a ring of NST LDS stages shared by the NW waves (NST-1 steps in flight);
-// each wave owns 16 heads (the query columns of its 16x16x32 MFMAs) and the
-// whole value width. When the value is a prefix of the key row (VK) the rows
-// are loaded once and the value operand is read from the key stage. A key is
-// live iff its position is at or before the token's.
-//
-// Stage layout: 32 rows at a pitch of one row (DK*2 bytes, 128 mod 256), so
-// each 1 KB direct load reads contiguous global memory. Row r stores its
-// logical 16-byte chunk c at c ^ sw(r) (sw(r) < 8 permutes within aligned
-// groups of 8 chunks), and every address is one of a few per-lane bases plus
-// an immediate:
-//   K operand: a 128-bit read of one chunk by 16 consecutive rows;
-//   V^T operand: a transposing read of 4 consecutive rows x 32 bytes.
-// The LDS serves a 128-bit read to lanes 0-7 with 32-39 in one cycle (then
-// 8-15 with 40-47, ...) and a 64-bit read to 32 consecutive lanes; under that
-// grouping (measured with the bank-conflict counter on these exact address
-// patterns) sw(r) = r1 | (r1^r2) << 1 | (r2^r3) << 2 makes both reads
-// conflict-free. (A plain bit permutation left the K reads 2-way conflicted.)
-struct GatherParams {
-    const void* __restrict__ q;  // bf16, fp32 or fp16 (q_type)
-    const uint16_t* __restrict__ kc;
-    const uint16_t* __restrict__ vc;
-    float* __restrict__ ws_o;
-    float* __restrict__ ws_ml;
-    const int32_t* __restrict__ row_index;
-    const float* __restrict__ key_pos;
-    const int32_t* __restrict__ q_pos;
-    // token t's own key row at kc + kcur_off + t * row_stride, value row at vc + vcur_off + ...
-    // (element offsets from the cache bases, so every gather address derives from one base pointer)
-    long long kcur_off, vcur_off;
-    int has_cur;
-    int T, Hq, n_sel, n_split, split_len;
-    long long row_stride;  // elements
-    float c_score, c_tanh, c_cap;
-    int causal, softcap_on;
-    int q_type;
-};
-
-// keys per split the LDS index table holds: a split of up to 1024 selected keys, plus the
-// token's own row in the last split, rounded up to whole 32-key steps
-constexpr int kGatherMaxSplit = 1024 + 32;
-
-#ifndef ATTN_GPF_K
-#define ATTN_GPF_K 4  // K fragments read ahead of their MFMA
-#endif
-#ifndef ATTN_GPF_V
-#define ATTN_GPF_V 4  // V^T fragments read ahead of their MFMA
-#endif
-
-// Wait until at most `later` stages of LPS direct loads per wave are still in flight.
-template <int LPS>
-__device__ __forceinline__ void wait_stages(int later) {
-    if (later >= 2)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPS) : "memory");
-    else if (later == 1)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS) : "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-template <int DK, int DV, int NW, bool VK, bool F16, bool CAUSAL, bool SOFTCAP>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_gathered_split_kernel(GatherParams p) {
-    constexpr int NT = NW * 64;
-    constexpr int KQ = DK / 32;   // QK k-steps of 32 dims
-    constexpr int DBV = DV / 16;  // 16-column blocks of O^T
-    constexpr int PITCH = DK * 2;             // LDS row pitch (bytes), key and value stages alike
-    constexpr int NCH = DK / 8;               // 16-byte chunks per row
-    constexpr int SSTAGE = 32 * PITCH;        // one stage of 32 rows
-    constexpr int NSEG = SSTAGE / 1024;       // 1 KB direct loads per stage
-    constexpr int STAGE = SSTAGE * (VK ? 1 : 2);
-    constexpr int NST = VK ? 4 : 2;
-    constexpr int LPS = (NSEG / NW) * (VK ? 1 : 2);  // direct loads per wave per stage
-    static_assert(DK % 32 == 0 && DV % 64 == 0 && DV <= DK && PITCH % 128 == 0 && PITCH % 256 != 0, "shape");
-    static_assert(SSTAGE % 1024 == 0 && NSEG % NW == 0 && NCH % 8 == 0, "stage");
-    static_assert(NST * STAGE + 12 * kGatherMaxSplit <= 160 * 1024, "LDS");
-    static_assert(NW * 16 * (DV + 4) * 4 <= NST * STAGE, "output staging fits the stages");
-    __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
-    __shared__ long long skoff[kGatherMaxSplit];  // element offset of each key row from kc
-    __shared__ __attribute__((aligned(16))) float spos[kGatherMaxSplit];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, c16 = lane & 15;
-    const int split = blockIdx.x, hgrp = blockIdx.y, t = blockIdx.z;
-    const int start = split * p.split_len;
-    const int end = min(p.n_sel, start + p.split_len);
-    const int nsel = end - start;
-    // the last split also takes the token's own row (n_keys = n_prior + 1), always live
-    const int has_cur = (p.has_cur && split == p.n_split - 1) ? 1 : 0;
-    const int nk = nsel + has_cur;
-    const float qpos = (float)p.q_pos[t];
-
-    // this split's row indices and positions (one per thread per pass)
-    constexpr int IPT = (kGatherMaxSplit + NT - 1) / NT;
-    long long roff_r[IPT];
-    float pos_r[IPT];
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-        const int i = tid + u * NT;
-        roff_r[u] = 0;
-        pos_r[u] = 0.f;
-        if (i < nsel) {
-            roff_r[u] = (long long)p.row_index[(size_t)t * p.n_sel + start + i];
-            pos_r[u] = p.key_pos[(size_t)t * p.n_sel + start + i];
-        }
-    }
-    // key rows as element offsets from kc (the token's own row from kcur), and positions
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-        const int i = tid + u * NT;
-        if (i < nsel) {
-            skoff[i] = roff_r[u] * p.row_stride;
-            spos[i] = pos_r[u];
-        }
-    }
-    if (has_cur && tid == 0) {
-        skoff[nsel] = p.kcur_off + (long long)t * p.row_stride;
-        spos[nsel] = qpos;
-    }
-    __syncthreads();
-
-    // query fragments (first needed by the first step's QK, so their latency hides
-    // under the first stages' copies)
-    const int h = hgrp * (NW * 16) + wave * 16 + c16;
-    const bool hok = h < p.Hq;
-    bf16x8 qf[KQ];
-    {
-        const size_t qrow = ((size_t)t * p.Hq + (hok ? h : 0)) * DK;
-#pragma unroll
-        for (int kk = 0; kk < KQ; ++kk) {
-            qf[kk] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-            if (hok) qf[kk] = load_q8<F16>(p.q, qrow + kk * 32 + grp * 8, p.q_type);
-        }
-    }
-
-    // row r stores logical chunk c at chunk c ^ sw(r) (within aligned groups of 8)
-    auto sw = [](int r) { return ((r >> 1) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 2); };
-    // Rows of step i into stage st: wave w fills 1 KB segments w, w+NW, ... All row offsets
-    // of the step are read from LDS before the first copy is issued (a copy writes LDS, so a
-    // later table read could not be moved ahead of it).
-    constexpr int JW = NSEG / NW;
-    auto issue = [&](int i, int st) {
-        char* sb = smem + st * STAGE;
-        long long ro[JW];
-        int kr[JW];
-#pragma unroll
-        for (int j = 0; j < JW; ++j) {
-            const int r = ((wave + j * NW) * 1024 + lane * 16) / PITCH;
-            kr[j] = min(i * 32 + r, nk - 1);
-            ro[j] = skoff[kr[j]];
-        }
-#pragma unroll
-        for (int j = 0; j < JW; ++j) {
-            const int sg = wave + j * NW;
-            const int off = sg * 1024 + lane * 16;
-            const int r = off / PITCH;
-            const int c = ((off - r * PITCH) >> 4) ^ sw(r);
-            load_lds16(p.kc + ro[j] + c * 8, sb + sg * 1024);
-            if constexpr (!VK) {
-                // value rows use the same layout; chunks past the value width repeat earlier ones
-                const long long vo = ro[j] + ((has_cur && kr[j] == nsel) ? p.vcur_off - p.kcur_off : 0);
-                load_lds16(p.vc + vo + (c % (DV / 8)) * 8, sb + SSTAGE + sg * 1024);
-            }
-        }
-    };
-
-    // per-lane LDS byte offsets within a stage
-    const int sk = sw(c16);  // rows c16 and c16 + 16
-    const int kofs0 = c16 * PITCH + ((grp ^ sk) << 4);        // even k-steps (+ kk/2 * 128)
-    const int kofs1 = c16 * PITCH + (((4 + grp) ^ sk) << 4);  // odd k-steps
-    const int ra = grp * 4 + (c16 >> 2);
-    const int sv = sw(ra);
-    const int xv = (c16 & 3) >> 1, bv = (c16 & 1) * 8;
-    int vofs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) vofs[j] = ra * PITCH + (((2 * j + xv) ^ sv) << 4) + bv;
-
-    f32x4 oacc[DBV];
-#pragma unroll
-    for (int d = 0; d < DBV; ++d) oacc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-
-    const int nsteps = (nk + 31) / 32;
-    for (int j = 0; j < NST - 1 && j < nsteps; ++j) issue(j, j);
-#pragma clang loop unroll(disable)
-    for (int i = 0; i < nsteps; ++i) {
-        wait_stages<LPS>(min(NST - 2, nsteps - 1 - i));
-        __syncthreads();
-        if (i + NST - 1 < nsteps) issue(i + NST - 1, (i + NST - 1) % NST);
-        __builtin_amdgcn_sched_barrier(0);
-        const char* kt = smem + (i % NST) * STAGE;
-        const char* vt = VK ? kt : kt + SSTAGE;
-        const int r0 = i * 32;
-        f32x4 kpos[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        if constexpr (CAUSAL) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) kpos[kb] = *(const f32x4*)(spos + r0 + kb * 16 + grp * 4);
-        }
-
-        constexpr int NQK = 2 * KQ;
-        constexpr int PFK = NQK < ATTN_GPF_K ? NQK : ATTN_GPF_K;
-        auto kload = [&](int idx) -> bf16x8 {
-            const int kk = idx >> 1, kb = idx & 1;
-            const int o = ((kk & 1) ? kofs1 : kofs0) + (kk >> 1) * 128 + kb * 16 * PITCH;
-            return *(const bf16x8*)(kt + o);
-        };
-        f32x4 sacc[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sacc[kb][0] = sacc[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bf16x8 kring[PFK];
-#pragma unroll
-        for (int j = 0; j < PFK; ++j) kring[j] = kload(j);
-#pragma unroll
-        for (int idx = 0; idx < NQK; ++idx) {
-            const bf16x8 a = kring[idx % PFK];
-            if (idx + PFK < NQK) kring[idx % PFK] = kload(idx + PFK);
-            const int kk = idx >> 1, kb = idx & 1;
-            sacc[kb][kk & 1] = mma16<F16>(a, qf[kk], sacc[kb][kk & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        f32x4 sc[2];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sc[kb] = sacc[kb][0] + sacc[kb][1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float x = sc[kb][e];
-                if constexpr (SOFTCAP) {
-                    const float ex = exp2_fast(x * p.c_tanh);
-                    x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(ex + 1.f);
-                } else {
-                    x *= p.c_score;
-                }
-                const int kl = r0 + kb * 16 + grp * 4 + e;  // key within the split
-                const bool live = kl < nk && (!CAUSAL || kpos[kb][e] <= qpos);
-                if (!live) x = -INFINITY;
-                sc[kb][e] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
-        mx = quarterwave_max(mx);
-        const bool upd = mx > m_run + kTau;
-        if (__builtin_amdgcn_ballot_w64(upd)) {
-            const float alpha = upd ? exp2_fast(m_run - mx) : 1.f;
-            m_run = upd ? mx : m_run;
-            l_run *= alpha;
-#pragma unroll
-            for (int d = 0; d < DBV; ++d) oacc[d] *= alpha;
-        }
-        const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-        uint32_t pk[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            pk[2 * kb] = pack_op2<F16>(exp2_fast(sc[kb][0] + nm), exp2_fast(sc[kb][1] + nm));
-            pk[2 * kb + 1] = pack_op2<F16>(exp2_fast(sc[kb][2] + nm), exp2_fast(sc[kb][3] + nm));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) l_run = add_op2<F16>(pk[j], l_run);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-
-        constexpr int PFV = DBV < ATTN_GPF_V ? DBV : ATTN_GPF_V;
-        auto vload = [&](int d) -> bf16x8 {
-            const char* pa = vt + vofs[d & 3] + (d >> 2) * 128;
-            const bf16x4 va = lds_read_tr16(pa);
-            const bf16x4 vb = lds_read_tr16(pa + 16 * PITCH);  // rows + 16
-            return __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-        };
-        bf16x8 vring[PFV];
-#pragma unroll
-        for (int j = 0; j < PFV; ++j) vring[j] = vload(j);
-#pragma unroll
-        for (int d = 0; d < DBV; ++d) {
-            const bf16x8 a = vring[d % PFV];
-            if (d + PFV < DBV) vring[d % PFV] = vload(d + PFV);
-            oacc[d] = mma16<F16>(a, pb, oacc[d]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    const float l_tot = quarterwave_sum(l_run);
-    if (hok && grp == 0) {
-        const size_t slot = ((size_t)t * p.Hq + h) * p.n_split + split;
-        p.ws_ml[slot * 2] = m_run;
-        p.ws_ml[slot * 2 + 1] = l_tot;
-    }
-    // Partial O through LDS (the stages are free once every wave is past its last step), so
-    // each store instruction writes 1 KB of contiguous partial row: the wave's 16 heads at a
-    // row pitch of DV + 4 floats (conflict-free writes of the O^T fragments).
-    constexpr int OP = DV + 4;
-    __syncthreads();
-    float* ost = (float*)smem + wave * 16 * OP;
-#pragma unroll
-    for (int d = 0; d < DBV; ++d) *(f32x4*)(ost + c16 * OP + d * 16 + grp * 4) = oacc[d];
-    // (a wave's LDS accesses complete in order, so it reads its own writes back directly)
-#pragma unroll 4
-    for (int k = 0; k < 16 * DV / 256; ++k) {  // 256 floats per instruction
-        const int hh = (k * 256) / DV, col = (k * 256) % DV + lane * 4;
-        const int head = hgrp * (NW * 16) + wave * 16 + hh;
-        if (head < p.Hq) {
-            const size_t slot = ((size_t)t * p.Hq + head) * p.n_split + split;
-            *(f32x4*)(p.ws_o + slot * DV + col) = *(const f32x4*)(ost + hh * OP + col);
-        }
-    }
-}
-
 struct CombineParams {
-    const float* __restrict__ ws_o;
+    const void* __restrict__ ws_o;  // fp32 O_s (paged) or bf16 O_s / l_s (gathered)
     const float* __restrict__ ws_ml;
     const int32_t* __restrict__ seq_lens;  // paged: bounds the splits to read; NULL: all splits
     const float* __restrict__ sinks;
@@ -656,7 +347,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
         nv = min(p.n_split, (L + p.split_len - 1) / p.split_len);
     }
     const float* ml = p.ws_ml + row * p.n_split * 2;
-    const float* ob = p.ws_o + row * p.n_split * p.dv;
+    const float* ob = (const float*)p.ws_o + row * p.n_split * p.dv;
     const int ncg = p.dv >> 2;  // 4-column groups
     // lane -> column groups c0 (+64) and split phase ph of G
     const int G = ncg >= 64 ? 1 : 64 / ncg;
@@ -735,6 +426,65 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
     }
 }
 
+// Combine of the gathered mode's ranges: the partial rows are 512 bf16 columns holding O_s / l_s,
+// merged with weights l_s e^{m_s - M}. One wavefront per output row (token, head); lane i owns
+// columns 8i .. 8i+7 (one 16-byte load per range). The first 8 ranges are loaded before the
+// range maxima are read; further ranges follow 8 at a time (indices clamped, weights of
+// missing ranges zero).
+template <bool OF32>
+__global__ __launch_bounds__(64) void decode_combine_norm_kernel(CombineParams p) {
+    constexpr int DV = 512, U = 8;
+    const int lane = threadIdx.x;
+    const size_t row = blockIdx.x;
+    const int h = (int)(row % p.Hq);
+    const int nv = p.n_split;
+    const float* ml = p.ws_ml + row * nv * 2;
+    const uint16_t* ob = (const uint16_t*)p.ws_o + row * nv * DV + lane * 8;
+    u32x4 x[U];
+    auto load_batch = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = *(const u32x4*)(ob + (size_t)min(s0 + u, nv - 1) * DV);
+    };
+    load_batch(0);
+    float M = -INFINITY;
+    for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const bool has_sink = p.sinks != nullptr;
+    const float sink2 = has_sink ? p.sinks[h] * kLog2e : -INFINITY;
+    const float M2 = fmaxf(M, sink2);
+    const float Mu = (M2 == -INFINITY) ? 0.f : M2;
+    float l = 0.f;
+    for (int s = lane; s < nv; s += 64) l += ml[2 * s + 1] * exp2_fast(ml[2 * s] - Mu);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (has_sink) l += exp2_fast(sink2 - Mu);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nv; s0 += U) {
+        if (s0 != 0) load_batch(s0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = min(s0 + u, nv - 1);
+            const float w = (s0 + u < nv) ? ml[2 * s + 1] * exp2_fast(ml[2 * s] - Mu) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] += w * bf16lo_to_f32(x[u][e]);
+                acc[2 * e + 1] += w * bf16hi_to_f32(x[u][e]);
+            }
+        }
+    }
+    if constexpr (OF32) {
+        float* o = (float*)p.o + row * DV + lane * 8;
+        *(f32x4*)o = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+        *(f32x4*)(o + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    } else {
+        *(u32x4*)((uint16_t*)p.o + row * DV + lane * 8) =
+            u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                  pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    }
+}
+
 // Query columns per workgroup: 16 (one MFMA block) at head dims >= 192, whose registers
 // are full, else up to 32; more columns take more workgroups.
 inline int paged_cols(int dk, int nq) { return (dk >= 192 || nq <= 16) ? 16 : 32; }
@@ -752,32 +502,8 @@ hipError_t launch_paged(const SplitParams& sp, bool f16, dim3 grid, hipStream_t 
     return f16 ? launch_paged_t<DK, DV, true>(sp, grid, stream) : launch_paged_t<DK, DV, false>(sp, grid, stream);
 }
 
-template <int NW, bool VK, bool F16, bool CAUSAL, bool SOFTCAP>
-hipError_t launch_gathered_t(const GatherParams& gp, dim3 grid, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_gathered_split_kernel<576, 512, NW, VK, F16, CAUSAL, SOFTCAP>), grid, dim3(NW * 64), 0,
-                       stream, gp);
-    return hipGetLastError();
-}
-template <int NW, bool VK, bool F16>
-hipError_t launch_gathered_f(const GatherParams& gp, bool causal, bool softcap, dim3 grid, hipStream_t stream) {
-    if (causal)
-        return softcap ? launch_gathered_t<NW, VK, F16, true, true>(gp, grid, stream)
-                       : launch_gathered_t<NW, VK, F16, true, false>(gp, grid, stream);
-    return softcap ? launch_gathered_t<NW, VK, F16, false, true>(gp, grid, stream)
-                   : launch_gathered_t<NW, VK, F16, false, false>(gp, grid, stream);
-}
-template <int NW>
-hipError_t launch_gathered(const GatherParams& gp, bool vk, bool f16, bool causal, bool softcap, dim3 grid,
-                           hipStream_t stream) {
-    if (vk)
-        return f16 ? launch_gathered_f<NW, true, true>(gp, causal, softcap, grid, stream)
-                   : launch_gathered_f<NW, true, false>(gp, causal, softcap, grid, stream);
-    return f16 ? launch_gathered_f<NW, false, true>(gp, causal, softcap, grid, stream)
-               : launch_gathered_f<NW, false, false>(gp, causal, softcap, grid, stream);
-}
-
-hipError_t launch_combine(const DecodeArgs& a, const DecodePlan& pl, float* ws_o, float* ws_ml,
-                          const int32_t* seq_lens, hipStream_t stream) {
+hipError_t launch_combine(const DecodeArgs& a, const DecodePlan& pl, void* ws_o, float* ws_ml,
+                          const int32_t* seq_lens, bool norm, hipStream_t stream) {
     CombineParams cp;
     cp.ws_o = ws_o;
     cp.ws_ml = ws_ml;
@@ -789,10 +515,19 @@ hipError_t launch_combine(const DecodeArgs& a, const DecodePlan& pl, float* ws_o
     cp.n_split = pl.n_split;
     cp.split_len = pl.split_len;
     cp.dv = a.dv;
-    if (a.o_f32)
-        hipLaunchKernelGGL((decode_combine_kernel<true>), dim3((unsigned)pl.n_rows), dim3(64), 0, stream, cp);
-    else
-        hipLaunchKernelGGL((decode_combine_kernel<false>), dim3((unsigned)pl.n_rows), dim3(64), 0, stream, cp);
+    const dim3 grid((unsigned)pl.n_rows);
+    if (norm) {  // gathered mode: dv is 512
+        if (a.dv != 512) return hipErrorInvalidValue;
+        if (a.o_f32)
+            hipLaunchKernelGGL((decode_combine_norm_kernel<true>), grid, dim3(64), 0, stream, cp);
+        else
+            hipLaunchKernelGGL((decode_combine_norm_kernel<false>), grid, dim3(64), 0, stream, cp);
+    } else {
+        if (a.o_f32)
+            hipLaunchKernelGGL((decode_combine_kernel<true>), grid, dim3(64), 0, stream, cp);
+        else
+            hipLaunchKernelGGL((decode_combine_kernel<false>), grid, dim3(64), 0, stream, cp);
+    }
     return hipGetLastError();
 }
 
@@ -811,10 +546,16 @@ bool decode_supported(int dk, int dv, bool gathered) {
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int dv) {
     DecodePlan pl;
-    if (dk == 576 && dv == 512) {
-        // gathered rows: one split per 8 MFMA steps of the 64-head workgroups up to 2048
-        // selected keys, longer splits beyond (at most the LDS index table of a split)
-        pl.split_len = Sk_max >= 16384 ? 1024 : Sk_max >= 4096 ? 512 : 256;
+    const bool gathered = dk == 576 && dv == 512;
+    if (gathered) {
+        // gathered rows: one workgroup per (token, 64 heads, key range). Aim for about 256
+        // workgroups (one per CU) with ranges of 64..1024 keys (the LDS index table of a range)
+        const long long units = (long long)B * gathered_head_groups(Hq);
+        const long long want = (256 + units - 1) / units;  // ranges per unit
+        const long long len = Sk_max > 0 ? (Sk_max + want - 1) / want : 64;
+        int sl = 64;
+        while (sl < len && sl < 1024) sl <<= 1;
+        pl.split_len = sl;
     } else {
         // paged: one wavefront per (split, KV head, sequence). Aim for about 4096 of them
         // (two rounds of two waves per SIMD) with splits of 256..2048 (4096) keys: long splits
@@ -832,7 +573,8 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
     }
     pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;
     pl.n_rows = (int64_t)B * Sq * Hq;
-    pl.ws_bytes = (size_t)pl.n_rows * pl.n_split * ((size_t)dv + 2) * sizeof(float);
+    // partial rows (fp32 O_s, or bf16 O_s / l_s for gathered rows), then (max, sum) per row and split
+    pl.ws_bytes = (size_t)pl.n_rows * pl.n_split * ((size_t)dv * (gathered ? 2 : 4) + 2 * sizeof(float));
     pl.ws_bytes = (pl.ws_bytes + 255) & ~(size_t)255;
     return pl;
 }
@@ -906,36 +648,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
 
     hipError_t e;
     if (a.row_index != nullptr) {
-        GatherParams gp;
-        gp.q = a.q;
-        gp.q_type = a.q_type;
-        gp.kc = (const uint16_t*)a.k_cache;
-        gp.vc = (const uint16_t*)a.v_cache;
-        gp.ws_o = ws_o;
-        gp.ws_ml = ws_ml;
-        gp.row_index = a.row_index;
-        gp.key_pos = a.key_pos;
-        gp.q_pos = a.q_pos;
-        gp.has_cur = a.k_cur != nullptr;
-        gp.kcur_off = gp.has_cur ? (long long)((const uint16_t*)a.k_cur - (const uint16_t*)a.k_cache) : 0;
-        gp.vcur_off = gp.has_cur ? (long long)((const uint16_t*)a.v_cur - (const uint16_t*)a.v_cache) : 0;
-        gp.T = a.B;
-        gp.Hq = a.Hq;
-        gp.n_sel = a.n_sel;
-        gp.n_split = pl.n_split;
-        gp.split_len = pl.split_len;
-        gp.row_stride = a.row_stride;
-        gp.c_score = sp.c_score;
-        gp.c_tanh = sp.c_tanh;
-        gp.c_cap = sp.c_cap;
-        gp.causal = a.causal;
-        gp.softcap_on = sp.softcap_on;
-        constexpr int NW = 4;
-        const dim3 ggrid((unsigned)pl.n_split, (unsigned)((a.Hq + NW * 16 - 1) / (NW * 16)), (unsigned)a.B);
-        const bool vk = a.v_cache == a.k_cache;
-        e = launch_gathered<NW>(gp, vk, a.kv_f16 != 0, a.causal != 0, sp.softcap_on != 0, ggrid, stream);
+        uint16_t* ws_on = (uint16_t*)a.workspace;
+        float* ws_mln = (float*)(ws_on + (size_t)pl.n_rows * pl.n_split * a.dv);
+        e = launch_gathered_split(a, pl, ws_on, ws_mln, stream);
         if (e != hipSuccess) return e;
-        return launch_combine(a, pl, ws_o, ws_ml, nullptr, stream);
+        return launch_combine(a, pl, ws_on, ws_mln, nullptr, true, stream);
     }
     const dim3 grid((unsigned)(a.Hkv * sp.ncg), (unsigned)a.B, (unsigned)pl.n_split);
     switch (a.dk * 1000 + a.dv) {
@@ -951,7 +668,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     }
     if (e != hipSuccess) return e;
 
-    return launch_combine(a, pl, ws_o, ws_ml, a.seq_lens, stream);
+    return launch_combine(a, pl, ws_o, ws_ml, a.seq_lens, false, stream);
 }
 
 }  // namespace attn

@@ -131,8 +131,8 @@ def decode(lib, **kw):
     (dict(Sq=1 << 12, Hq=512, Hkv=1), 2),                   # 2^21 query columns per KV head
     (dict(B=65536), 2),                                     # B is a grid dimension of at most 65535
     (dict(B=1024, Hq=1 << 16, Hkv=1 << 16), 2),             # 2^26 output rows for the combine
-    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=100, stride=576, dk=576, dv=512,
-          Hq=65536 * 64), 2),                               # 65536 groups of 64 heads
+    (dict(table=None, rows=FAKE, kpos=FAKE, qpos=FAKE, n_sel=1 << 23, Sk_max=1 << 23, stride=576, dk=576,
+          dv=512, B=256, Hq=128 * 2047), 2),                # 256 * 2047 head groups * 8192 ranges >= 2^31
     (dict(kcur=FAKE, vcur=FAKE), 1),                        # current rows in paged mode
     (dict(qd=5), 1),                                        # unknown q dtype
     (dict(kvd=1), 1),                                       # fp32 caches are not an operand type
@@ -160,9 +160,10 @@ def test_workspace_bytes():
     # one sequence: 256-key splits keep about 4096 wavefronts busy
     n = attn.attn_decode_workspace_bytes(1, 8, 8, 1, 16384, 128, 128)
     assert n >= 1 * 8 * 64 * 130 * 4
-    # 2048 keys use 256-key splits: 8 splits
+    # gathered, 16 tokens x 128 heads (2 groups of 64) x 2048 keys: 8 ranges of 256 keys give
+    # 256 workgroups; bf16 rows (dv * 2 bytes) plus fp32 (max, sum) per row per range
     n = attn.attn_decode_workspace_bytes(16, 128, 1, 1, 2048, 576, 512)
-    assert n >= 16 * 128 * 8 * 514 * 4
+    assert n == (16 * 128 * 8 * (512 * 2 + 8) + 255) // 256 * 256
     assert attn.attn_decode_workspace_bytes(0, 64, 8, 1, 100, 128, 128) == 0
     assert attn.attn_decode_workspace_bytes(2, 6, 4, 1, 100, 128, 128) == 0
     # past the launch limits (2^26 output rows; B above 65535): no workspace size
