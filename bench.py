@@ -6,20 +6,22 @@ U{1024..32768}, 64-token blocks placed by a random block table: split kernel +
 combine). Inputs are seeded synthetic tensors resident in HBM before timing.
 
 The JSON line's `value` is prefill TFLOP/s (algorithmic flops: only the
-visible causal pairs, 4*d flops each), timed with HIP events on the stream the
-kernels run on; the decode half of the metric (algorithmic KV bytes per
-second) is in `decode`. Other workloads (GQA d=256 with and without
-causal+softcap+sinks, single-head d=16) are timed after the step loop and
-reported under `other`. `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the prefill workload.
+visible causal pairs, 2*(dk+dv) flops each), timed with HIP events on the
+stream the kernels run on; the decode half of the metric (algorithmic KV bytes
+per second) is in `decode`. `workloads` holds every one of the five
+workloads (single head d=16; causal MHA d=128; GQA d=256 plain and with
+causal + softcap + sinks; paged GQA decode; gathered MLA decode), each with
+its kernels, time, rate, roofline fraction and counter-measured traffic; the
+ones outside the step are timed after the step loop. `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of each workload.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu] [--no-other] [--gpus 1]
 """
 
 import argparse
 import json
-import math
 import os
+import subprocess
 import sys
 import time
 
@@ -35,39 +37,154 @@ METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM pe
 
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE passes (read counter
 # scaled x2, write x1 against a 1 GiB plain copy; see profiles/hbm_traffic_bench.md), valid
-# only while the kernel sources hash to the values they were measured on.
+# only while the kernel sources and build options hash to the values they were measured on.
+_PREFILL_SRC = ("prefill.hip", "attn_device.hpp", "../build.py")
+_D256_SRC = ("prefill.hip", "prefill_d256.hip", "attn_device.hpp", "../build.py")
+_DECODE_SRC = ("decode.hip", "attn_device.hpp", "../build.py")
+_GATHER_SRC = ("decode.hip", "decode_gathered.hip", "attn_device.hpp", "../build.py")
 MEASURED_TRAFFIC = {
-    "prefill_c2": {"sources": ("prefill.hip", "attn_device.hpp", "../build.py"), "sha256_16": "0faed732a068c308", "bytes": 653849049},
-    "decode_c4": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "4ca49410d0a34b75", "bytes": 5035204832},
-    "decode_c5": {"sources": ("decode.hip", "attn_device.hpp", "../build.py"), "sha256_16": "4ca49410d0a34b75", "bytes": 123606018},
+    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "", "bytes": None},
+    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "", "bytes": None},
+    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "", "bytes": None},
+    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "", "bytes": None},
+    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "", "bytes": None},
 }
+
+
+def sources_hash(files):
+    import hashlib
+    m = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "attention_flash_attn_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
 
 
 def measured_traffic(key):
     """The recorded traffic if the kernel sources and build options (build.py) are unchanged
     since the counters were taken."""
-    import hashlib
-    e = MEASURED_TRAFFIC[key]
-    m = hashlib.sha256()
-    for f in e["sources"]:
-        with open(os.path.join(ROOT, "attention_flash_attn_amd", "csrc", f), "rb") as fh:
-            m.update(fh.read())
-    return e["bytes"] if m.hexdigest()[:16] == e["sha256_16"] else None
+    e = MEASURED_TRAFFIC.get(key)
+    if e is None or e["bytes"] is None:
+        return None
+    return e["bytes"] if sources_hash(e["sources"]) == e["sha256_16"] else None
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def prefill_flops(c):
-    """Algorithmic flops: 2*(dk+dv) per visible (query, key) pair."""
-    B, Sq, Sk, Hq = c["B"], c["Sq"], c["Sk"], c["Hq"]
+def prefill_pairs(c, rows=None):
+    """Visible (query, key) pairs of one (batch, head), over the given query rows."""
+    Sq, Sk = c["Sq"], c["Sk"]
+    rows = range(Sq) if rows is None else rows
     if c["causal"]:
         shift = Sk - Sq
-        pairs = sum(max(0, min(Sk, i + shift + 1)) for i in range(Sq))
-    else:
-        pairs = Sq * Sk
-    return 2.0 * (c["dk"] + c["dv"]) * pairs * B * Hq
+        return sum(max(0, min(Sk, i + shift + 1)) for i in rows)
+    return len(rows) * Sk
+
+
+def prefill_flops(c):
+    """Algorithmic flops: 2*(dk+dv) per visible (query, key) pair."""
+    return 2.0 * (c["dk"] + c["dv"]) * prefill_pairs(c) * c["B"] * c["Hq"]
+
+
+def host_info():
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "Model name":
+                info["lscpu_model"] = v
+            elif k == "CPU(s)":
+                info["lscpu_cpus"] = int(v)
+            elif k == "Thread(s) per core":
+                info["lscpu_threads_per_core"] = int(v)
+    except Exception as e:  # lscpu missing: report what os.cpu_count() says
+        info["lscpu_error"] = str(e)
+    return info
+
+
+def cpu_baselines(repeats):
+    """The fp64 oracle (as it stands) on a bounded sample of each workload, on the host's
+    cores: all BLAS threads, plus one thread for the single-head and gathered workloads.
+    Median of `repeats` runs (one if a run takes over 60 s)."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from attention_flash_attn_amd import synth
+
+    blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+
+    def timed(fn):
+        ts = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+            if ts[-1] > 60.0:
+                break
+        return float(np.median(ts)), len(ts)
+
+    out = {}
+    # prefill workloads: all query rows of a subset of (batch, head) pairs
+    samples = {"c1_single_head_d16": 1, "c2_causal_mha_d128": 16, "c3a_gqa_d256": 8,
+               "c3b_gqa_d256_causal_softcap": 8}
+    for name, nh in samples.items():
+        c = synth.CONFIGS[name]
+        cc = synth.prefill_case(c["seed"], c["B"], c["Sq"], c["Sk"], c["Hq"], c["Hkv"], c["dk"], c["dv"],
+                                std=c["std"], sinks=c["sinks"])
+        heads = list(range(nh))
+
+        def run(cc=cc, c=c, heads=heads):
+            oracle.prefill(cc["q"], cc["k"], cc["v"], c["scale"], causal=c["causal"], softcap=c["softcap"],
+                           sinks=cc["sinks"], heads=heads, batches=[0])
+        flops = 2.0 * (c["dk"] + c["dv"]) * prefill_pairs(c) * nh
+        for threads in ([blas, 1] if name.startswith("c1") else [blas]):
+            with threadpool_limits(limits=threads, user_api="blas"):
+                t, n = timed(run)
+            key = name if threads == blas else name + "_1core"
+            out[key] = {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                        "seconds": round(t, 4), "runs": n,
+                        "sample": "%d of the %d (batch, head) pairs, all %d query rows (%.3g flop)" %
+                                  (nh, c["B"] * c["Hq"], c["Sq"], flops)}
+        log("oracle %s: %.2f s -> %.4f TFLOP/s" % (name, out[name]["seconds"], out[name]["value"]))
+        del cc
+    # paged decode: 16 of the 64 sequences
+    c = synth.CONFIGS["c4_paged_gqa_decode"]
+    pc = synth.paged_case(c["seed"], c["B"], c["Hq"], c["Hkv"], c["dk"], c["dv"], c["len_lo"], c["len_hi"],
+                          block_size=c["block_size"])
+    nb = 16
+    kv_bytes = float(pc["seq_lens"][:nb].astype(np.int64).sum()) * c["Hkv"] * (c["dk"] + c["dv"]) * 2
+    t, n = timed(lambda: oracle.decode_paged(pc["q"], pc["k_cache"], pc["v_cache"], pc["block_table"],
+                                             pc["seq_lens"], c["scale"], batches=list(range(nb))))
+    out["c4_paged_gqa_decode"] = {"value": round(kv_bytes / t / 1e9, 4), "unit": "GB/s", "cores": blas,
+                                  "kind": "oracle", "seconds": round(t, 4), "runs": n,
+                                  "sample": "%d of the %d sequences (%.3g B of K/V)" % (nb, c["B"], kv_bytes)}
+    log("oracle c4: %.2f s -> %.3f GB/s" % (t, out["c4_paged_gqa_decode"]["value"]))
+    del pc
+    # gathered decode: all 16 tokens
+    c = synth.CONFIGS["c5_gathered_mla_decode"]
+    gc = synth.gathered_case(c["seed"], c["T"], c["Hq"], c["dk"], c["dv"], c["n_rows"], c["n_sel"],
+                             row_dim=c["row_dim"])
+    kv = gc["kv"]
+    rows_bytes = float(c["T"] * c["n_sel"] * c["row_dim"] * 2)
+
+    def run5():
+        oracle.decode_gathered(gc["q"], kv[:, :c["dk"]], kv[:, :c["dv"]], gc["row_index"], gc["key_pos"],
+                               gc["q_pos"], c["scale"], causal=True)
+    for threads in (blas, 1):
+        with threadpool_limits(limits=threads, user_api="blas"):
+            t, n = timed(run5)
+        key = "c5_gathered_mla_decode" + ("" if threads == blas else "_1core")
+        out[key] = {"value": round(rows_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                    "seconds": round(t, 4), "runs": n,
+                    "sample": "all %d tokens x %d heads x %d selected rows (%.3g B of rows)" %
+                              (c["T"], c["Hq"], c["n_sel"], rows_bytes)}
+    log("oracle c5: %.2f s -> %.3f GB/s" % (out["c5_gathered_mla_decode"]["seconds"],
+                                            out["c5_gathered_mla_decode"]["value"]))
+    return out
 
 
 def main():
@@ -79,8 +196,8 @@ def main():
                     help="seconds of untimed steps run before the warm-up steps, so the GPU clock reaches its "
                          "steady state whatever --warmup is (0 = none); reported as settle_s")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-other", action="store_true", help="skip the extra workloads")
-    ap.add_argument("--cpu-heads", type=int, default=64, help="(batch, head) pairs in the CPU sample")
+    ap.add_argument("--no-other", action="store_true", help="skip the workloads outside the step and the variants")
+    ap.add_argument("--cpu-repeats", type=int, default=3, help="oracle runs per CPU sample (median reported)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a plain copy kernel of known size, "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -96,11 +213,31 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    # ---------------- inputs (seeded, synthetic), resident in HBM
+    def event_time(fn, reps):
+        """Mean seconds per call of fn, reps calls between two HIP events on the kernels' stream."""
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        z.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) * 1e-3 / reps
+
+    def warm(fn, seconds):
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            fn(i)
+            i += 1
+            torch.cuda.synchronize()
+
+    # ---------------- inputs of the step (seeded, synthetic), resident in HBM
     c2 = synth.CONFIGS["c2_causal_mha_d128"]
     log("generating prefill inputs")
     pc = synth.prefill_case(c2["seed"], c2["B"], c2["Sq"], c2["Sk"], c2["Hq"], c2["Hkv"], c2["dk"], c2["dv"],
@@ -129,25 +266,18 @@ def main():
     io_bytes4 = (q4.numel() + o4.numel()) * 2 + table4.numel() * 4 + lens4.numel() * 4
     bytes4 = kv_bytes4 + io_bytes4
 
-    def prefill():
+    def prefill(_i=0):
         binding.attn_prefill_fwd(q2, k2, v2, o2, None, scale=c2["scale"], causal=True)
 
-    def decode():
+    def decode(_i=0):
         binding.attn_decode_fwd(q4, kc4, vc4, o4, ws4, scale=c4["scale"], Sk_max=c4["len_hi"],
                                 block_table=table4, seq_lens=lens4)
 
-    stream = torch.cuda.current_stream()
     if args.calib_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        dst.copy_(src)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        log("calibration copy: 1 GiB in %.1f us (%.0f GB/s read+write)" %
-            (c0.elapsed_time(c1) * 1e3, 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9))
+        t = event_time(lambda i: dst.copy_(src), 1)
+        log("calibration copy: 1 GiB in %.1f us (%.0f GB/s read+write)" % (t * 1e6, 2 * (1 << 30) / t / 1e9))
         del src, dst
     # clock settle: under this load the GPU clock needs ~0.1 s to reach its steady state, longer
     # than a few warm-up steps take, so full steps run untimed for a fixed time first
@@ -175,26 +305,39 @@ def main():
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_pre = [ev[i][0].elapsed_time(ev[i][1]) * 1e-3 for i in range(K)]
-    t_dec = [ev[i][1].elapsed_time(ev[i][2]) * 1e-3 for i in range(K)]
-    avg_pre = sum(t_pre) / K
-    avg_dec = sum(t_dec) / K
+    avg_pre = sum(ev[i][0].elapsed_time(ev[i][1]) * 1e-3 for i in range(K)) / K
+    avg_dec = sum(ev[i][1].elapsed_time(ev[i][2]) * 1e-3 for i in range(K)) / K
     tflops = flops2 / avg_pre / 1e12
     dec_gbs = bytes4 / avg_dec / 1e9
     log("prefill c2: %.1f us/launch, %.1f TFLOP/s (%.1f%% of peak)" % (avg_pre * 1e6, tflops,
                                                                         100 * tflops / PEAK_BF16_TFLOPS))
     # the same prefill launched back to back (no decode in between): sustained MFMA load
     # lowers the clock, so this is reported beside the in-step figure
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K):
-        prefill()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_b2b = e0.elapsed_time(e1) * 1e-3 / K
+    t_b2b = event_time(prefill, K)
     log("prefill c2 back to back: %.1f us/launch, %.1f TFLOP/s" % (t_b2b * 1e6, flops2 / t_b2b / 1e12))
     log("decode c4: %.1f us/call, %.1f GB/s (%.1f%% of peak)" % (avg_dec * 1e6, dec_gbs, 100 * dec_gbs / PEAK_HBM_GBS))
 
+    def entry(name, workload, kernels, seconds, work, bound, extra=None):
+        unit = "TFLOP/s" if bound == "mfma" else "GB/s"
+        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+        achieved = work / seconds / (1e12 if bound == "mfma" else 1e9)
+        e = {"workload": workload, "kernels": kernels, "us": round(seconds * 1e6, 2), "bound": bound,
+             "achieved": round(achieved, 2), "unit": unit, "peak": peak, "frac": round(achieved / peak, 4),
+             ("flops_per_launch" if bound == "mfma" else "bytes_per_call"): work,
+             "traffic": measured_traffic(name)}
+        if extra:
+            e.update(extra)
+        return e
+
+    workloads = {
+        "c2_causal_mha_d128": entry("c2_causal_mha_d128", "causal MHA prefill B=2 Hq=Hkv=32 Sq=Sk=4096 d=128, bf16 "
+                                    "out (in the step)", "prefill_kernel<128,128,64,8,2,causal>", avg_pre, flops2,
+                                    "mfma", {"back_to_back_us": round(t_b2b * 1e6, 2)}),
+        "c4_paged_gqa_decode": entry("c4_paged_gqa_decode", "paged GQA decode B=64 Hq=64 Hkv=8 d=128 lengths "
+                                     "U{1024..32768} 64-token blocks, bf16 out (in the step)",
+                                     "decode_paged_split_kernel<128,128,1> + decode_combine_kernel", avg_dec,
+                                     bytes4, "hbm"),
+    }
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -223,7 +366,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic("prefill_c2"),
+            "traffic": measured_traffic("c2_causal_mha_d128"),
             "avg_launch_us": round(avg_pre * 1e6, 2),
             "back_to_back_TFLOP/s": round(flops2 / t_b2b / 1e12, 2),
             "back_to_back_us": round(t_b2b * 1e6, 2),
@@ -234,8 +377,9 @@ def main():
             "us_per_call": round(avg_dec * 1e6, 2),
             "roofline": {"kernel": "decode_paged_split_kernel<128,128> + decode_combine_kernel", "bound": "hbm",
                          "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_c4")},
+                         "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("c4_paged_gqa_decode")},
         },
+        "workloads": workloads,
     }
 
     # ---------------- gathered-row decode (MLA shape), timed cold: 8 copies of the row
@@ -246,6 +390,7 @@ def main():
                              row_dim=c5["row_dim"])
     ncopy = 8
     kv5 = [to_dev(gc["kv"]) for _ in range(ncopy)]
+    rows5 = [(kv[:, :c5["dk"]], kv[:, :c5["dv"]]) for kv in kv5]
     q5 = to_dev(gc["q"]).view(c5["T"], 1, c5["Hq"], c5["dk"])
     ri5 = torch.from_numpy(gc["row_index"]).to(dev)
     kp5 = torch.from_numpy(gc["key_pos"]).to(dev)
@@ -258,38 +403,43 @@ def main():
     flops5 = 2.0 * c5["T"] * c5["Hq"] * c5["n_sel"] * (c5["dk"] + c5["dv"])
 
     def gathered(i):
-        kv = kv5[i % ncopy]
-        binding.attn_decode_fwd(q5, kv[:, :c5["dk"]], kv[:, :c5["dv"]], o5, ws5, scale=c5["scale"],
-                                Sk_max=c5["n_sel"], causal=True, row_index=ri5, key_pos=kp5, q_pos=qp5)
-    for i in range(ncopy):
-        gathered(i)
-    reps = 8 * ncopy
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(reps):
-        gathered(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t5 = e0.elapsed_time(e1) * 1e-3 / reps
-    log("gathered decode c5: %.2f us/call, %.1f GB/s (%.1f%% of HBM peak), %.1f TFLOP/s" %
-        (t5 * 1e6, bytes5 / t5 / 1e9, 100 * bytes5 / t5 / 1e9 / PEAK_HBM_GBS, flops5 / t5 / 1e12))
-    result["decode_gathered"] = {
-        "workload": "16 tokens x 128 heads, 2048 gathered rows of 576 (key) / first 512 (value), "
-                    "65536-row cache in permuted 64-row blocks, causal on position, bf16 out, cold (8 rotated "
-                    "cache copies)",
-        "value": round(bytes5 / t5 / 1e9, 1), "unit": "GB/s", "us_per_call": round(t5 * 1e6, 2),
-        "bytes_per_call": bytes5, "flops_per_call": flops5,
-        "roofline": {"kernel": "decode_gathered_split_kernel<576,512,4> + decode_combine_kernel", "bound": "hbm",
-                     "achieved": round(bytes5 / t5 / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(bytes5 / t5 / 1e9 / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_c5"),
-                     "mfma_frac": round(flops5 / t5 / 1e12 / PEAK_BF16_TFLOPS, 4)},
-    }
-    del kv5, gc
+        kr, vr = rows5[i % ncopy]
+        binding.attn_decode_fwd(q5, kr, vr, o5, ws5, scale=c5["scale"], Sk_max=c5["n_sel"], causal=True,
+                                row_index=ri5, key_pos=kp5, q_pos=qp5)
+    warm(gathered, 0.025)
+    t5 = event_time(gathered, 8 * ncopy)
+    # the same calls replayed from a captured HIP graph: the device time without host launch gaps
+    try:
+        graph5 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph5):
+            for i in range(ncopy):
+                gathered(i)
+        graph5.replay()
+        t5g = event_time(lambda i: graph5.replay(), 8) / ncopy
+        del graph5
+    except Exception as e:  # graph capture unavailable: report the eager time only
+        log("graph timing of c5 skipped: %s" % e)
+        t5g = float("nan")
+    log("gathered decode c5: %.2f us/call (%.2f from a graph), %.1f GB/s (%.1f%% of HBM peak), %.1f TFLOP/s" %
+        (t5 * 1e6, t5g * 1e6, bytes5 / t5 / 1e9, 100 * bytes5 / t5 / 1e9 / PEAK_HBM_GBS, flops5 / t5 / 1e12))
+    workloads["c5_gathered_mla_decode"] = entry(
+        "c5_gathered_mla_decode", "16 tokens x 128 heads, 2048 gathered rows of 576 (key) / first 512 (value), "
+        "65536-row cache in permuted 64-row blocks, causal on position, bf16 out, cold (8 rotated cache copies)",
+        "decode_gathered_kernel<576,512,true,false,true,false> + decode_combine_norm_kernel", t5, bytes5, "hbm",
+        {"flops_per_call": flops5, "mfma_frac": round(flops5 / t5 / 1e12 / PEAK_BF16_TFLOPS, 4),
+         "us_graph": None if t5g != t5g else round(t5g * 1e6, 2)})
+    del kv5, rows5, gc
 
-    # ---------------- other workloads (own timing, after the step loop)
+    # ---------------- the other prefill workloads (own timing, after the step loop)
     if not args.no_other:
-        other = {}
+        kernels = {"c3a_gqa_d256": "prefill_kernel<256,256,32,8,2,plain>",
+                   "c3b_gqa_d256_causal_softcap": "prefill_kernel<256,256,32,8,2,causal,softcap>",
+                   "c1_single_head_d16": "prefill_kernel<16,16,64,4,2,plain,fp32 out>"}
+        descs = {"c3a_gqa_d256": "GQA prefill B=1 Hq=64 Hkv=8 Sq=Sk=4096 d=256, no mask, sinks, bf16 out",
+                 "c3b_gqa_d256_causal_softcap": "GQA prefill B=1 Hq=64 Hkv=8 Sq=Sk=4096 d=256, causal, softcap 50, "
+                                                "sinks, bf16 out",
+                 "c1_single_head_d16": "single head B=1 H=1 Sq=Sk=128 d=16, fp32 out (correctness-sized; "
+                                       "launch-bound)"}
         for name in ("c3a_gqa_d256", "c3b_gqa_d256_causal_softcap", "c1_single_head_d16"):
             c = synth.CONFIGS[name]
             log("generating %s" % name)
@@ -300,45 +450,22 @@ def main():
             o = torch.empty((c["B"], c["Sq"], c["Hq"], c["dv"]), device=dev,
                             dtype=torch.float32 if c["o_dtype"] == "f32" else torch.bfloat16)
 
-            def run(q=q, k=k, v=v, o=o, sk=sk, c=c):
+            def run(_i=0, q=q, k=k, v=v, o=o, sk=sk, c=c):
                 binding.attn_prefill_fwd(q, k, v, o, None, scale=c["scale"], causal=c["causal"],
                                          softcap=c["softcap"], sinks=sk)
-            t0 = time.perf_counter()
-            while time.perf_counter() - t0 < 0.1:  # at least 100 ms of warm work: steady clocks
-                run()
-                torch.cuda.synchronize()
-            reps = 50
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(reps):
-                run()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t = e0.elapsed_time(e1) * 1e-3 / reps
-            f = prefill_flops(c)
-            other[name] = {"us": round(t * 1e6, 2), "TFLOP/s": round(f / t / 1e12, 2),
-                           "frac_bf16_peak": round(f / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
-            log("%s: %.1f us, %.1f TFLOP/s" % (name, t * 1e6, f / t / 1e12))
+            warm(run, 0.1)  # at least 100 ms of warm work: steady clocks
+            t = event_time(run, 50)
+            workloads[name] = entry(name, descs[name], kernels[name], t, prefill_flops(c), "mfma")
+            log("%s: %.1f us, %.1f TFLOP/s" % (name, t * 1e6, prefill_flops(c) / t / 1e12))
             del q, k, v, o, cc
-        result["other"] = other
 
         # the widened operations at the same workload shapes (own timing)
         def timed(fn, reps=10):
-            t0 = time.perf_counter()
-            while time.perf_counter() - t0 < 0.025:  # at least 25 ms of warm work: steady clocks
-                fn()
-                torch.cuda.synchronize()
-            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                fn()
-            z.record(stream)
-            torch.cuda.synchronize()
-            return a.elapsed_time(z) * 1e-3 / reps
+            warm(lambda i: fn(), 0.025)  # at least 25 ms of warm work: steady clocks
+            return event_time(lambda i: fn(), reps)
 
         variants = {}
-        log("variants: ALiBi mask, fp16 K/V, multi-token decode, q8_0 pre-pass")
+        log("variants: ALiBi mask, fp16 K/V, multi-token decode, q8_0 pre-pass, MLA tail")
         mask2 = torch.from_numpy(synth.mask_case(2, 1, 1, c2["Sq"], c2["Sk"], kind="distance")).to(dev)
         t = timed(lambda: binding.attn_prefill_fwd_ex(q2, k2, v2, o2, scale=c2["scale"], causal=True, mask=mask2,
                                                       max_bias=8.0))
@@ -400,28 +527,14 @@ def main():
             log("%s: %s" % (k, ", ".join("%s %s" % (a, b) for a, b in v.items() if a != "workload")))
         result["variants"] = variants
 
-    # ---------------- CPU baseline: the oracle on a bounded sample of the prefill workload
+    # ---------------- CPU baseline: the oracle on a bounded sample of each workload
     if not args.no_cpu:
-        import oracle
-        log("CPU oracle baseline")
-        pc = synth.prefill_case(c2["seed"], c2["B"], c2["Sq"], c2["Sk"], c2["Hq"], c2["Hkv"], c2["dk"], c2["dv"],
-                                std=c2["std"])
-        pairs = [(b, h) for b in range(c2["B"]) for h in range(c2["Hq"])][:args.cpu_heads]
-        t0 = time.perf_counter()
-        for b, h in pairs:
-            oracle.prefill(pc["q"], pc["k"], pc["v"], c2["scale"], causal=True, heads=[h], batches=[b])
-        tc = time.perf_counter() - t0
-        try:  # BLAS threads the oracle's matrix products ran on
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
-        except Exception:
-            cores = os.cpu_count() or 1
-        f = prefill_flops(c2) / (c2["B"] * c2["Hq"]) * len(pairs)
-        result["cpu_baseline"] = {"value": round(f / tc / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-                                  "kind": "oracle",
-                                  "sample": "%d of the 64 (batch, head) pairs of the causal MHA prefill "
-                                            "(4096 x 4096, d=128), fp64 numpy, %.1f s" % (len(pairs), tc)}
-        log("oracle: %.1f s for %d heads -> %.4f TFLOP/s" % (tc, len(pairs), f / tc / 1e12))
+        log("CPU oracle baseline (median of %d runs per sample)" % args.cpu_repeats)
+        per = cpu_baselines(args.cpu_repeats)
+        head = dict(per["c2_causal_mha_d128"])
+        head["per_config"] = per
+        head["host"] = host_info()
+        result["cpu_baseline"] = head
 
     print(json.dumps(result), flush=True)
 
