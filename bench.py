@@ -129,17 +129,19 @@ def cpu_baselines(repeats):
 
     out = {}
     # prefill workloads: all query rows of a subset of (batch, head) pairs
-    samples = {"c1_single_head_d16": 1, "c2_causal_mha_d128": 16, "c3a_gqa_d256": 8,
-               "c3b_gqa_d256_causal_softcap": 8}
+    samples = {"c1_single_head_d16": 1, "c2_causal_mha_d128": 64, "c3a_gqa_d256": 32,
+               "c3b_gqa_d256_causal_softcap": 32}
     for name, nh in samples.items():
         c = synth.CONFIGS[name]
         cc = synth.prefill_case(c["seed"], c["B"], c["Sq"], c["Sk"], c["Hq"], c["Hkv"], c["dk"], c["dv"],
                                 std=c["std"], sinks=c["sinks"])
-        heads = list(range(nh))
+        heads = list(range(min(nh, c["Hq"])))
+        batches = list(range(nh // len(heads)))
+        assert len(heads) * len(batches) == nh and len(batches) <= c["B"]
 
-        def run(cc=cc, c=c, heads=heads):
+        def run(cc=cc, c=c, heads=heads, batches=batches):
             oracle.prefill(cc["q"], cc["k"], cc["v"], c["scale"], causal=c["causal"], softcap=c["softcap"],
-                           sinks=cc["sinks"], heads=heads, batches=[0])
+                           sinks=cc["sinks"], heads=heads, batches=batches)
         flops = 2.0 * (c["dk"] + c["dv"]) * prefill_pairs(c) * nh
         for threads in ([blas, 1] if name.startswith("c1") else [blas]):
             with threadpool_limits(limits=threads, user_api="blas"):
@@ -151,11 +153,11 @@ def cpu_baselines(repeats):
                                   (nh, c["B"] * c["Hq"], c["Sq"], flops)}
         log("oracle %s: %.2f s -> %.4f TFLOP/s" % (name, out[name]["seconds"], out[name]["value"]))
         del cc
-    # paged decode: 16 of the 64 sequences
+    # paged decode: 32 of the 64 sequences
     c = synth.CONFIGS["c4_paged_gqa_decode"]
     pc = synth.paged_case(c["seed"], c["B"], c["Hq"], c["Hkv"], c["dk"], c["dv"], c["len_lo"], c["len_hi"],
                           block_size=c["block_size"])
-    nb = 16
+    nb = 32
     kv_bytes = float(pc["seq_lens"][:nb].astype(np.int64).sum()) * c["Hkv"] * (c["dk"] + c["dv"]) * 2
     t, n = timed(lambda: oracle.decode_paged(pc["q"], pc["k_cache"], pc["v_cache"], pc["block_table"],
                                              pc["seq_lens"], c["scale"], batches=list(range(nb))))
