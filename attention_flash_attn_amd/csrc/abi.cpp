@@ -311,9 +311,9 @@ attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blo
     if (n_blocks == 0) return ok();
     if (!src || !dst) return fail(ATTN_ERR_INVALID_ARG, "src and dst are required");
     if (!aligned16(src) || !aligned16(dst)) return fail(ATTN_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
-    // one thread per block in a 1-D grid of fewer than 2^32 threads (256 per workgroup)
-    if (n_blocks > ((int64_t)1 << 32) - 256)
-        return fail(ATTN_ERR_UNSUPPORTED, "n_blocks above 2^32 - 256: too many blocks for one launch");
+    // four threads per block in a 1-D grid of fewer than 2^32 threads (64 blocks per workgroup)
+    if (n_blocks > ((int64_t)1 << 30) - 64)
+        return fail(ATTN_ERR_UNSUPPORTED, "n_blocks above 2^30 - 64: too many blocks for one launch");
     hipError_t e = attn::launch_dequant(src, fmt, dst, (long long)n_blocks, (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "dequant launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -8,16 +8,17 @@
 // d * q is exact in fp32 (11 + 8 significand bits) and is rounded once to fp16
 // (nearest even).
 //
-// One 256-thread workgroup per 256 blocks: the packed bytes (8704 or 4608,
-// 16-byte aligned whenever the buffer is) are staged into LDS with 16-byte
-// loads, then thread i expands block i into 64 contiguous output bytes.
+// One 256-thread workgroup per 64 blocks: the packed bytes (2176 or 1152, 16-byte aligned
+// whenever the buffer is) are staged into LDS with 16-byte loads; then thread i expands values
+// 8 (i % 4) .. 8 (i % 4) + 7 of block i / 4 into 16 output bytes, so a wave stores 1 KB of
+// contiguous output per instruction.
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int kBlocksPerWG = 256;
+constexpr int kBlocksPerWG = 64;
 
 template <int BYTES>  // 34 (q8_0) or 18 (q4_0)
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ src, uint16_t* __restrict__ dst,
@@ -40,29 +41,33 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
         }
     }
     __syncthreads();
-    if (tid >= nb) return;
+    const int blk = tid >> 2, part = tid & 3;
+    if (blk >= nb) return;
 
-    const uint8_t* b = stage + tid * BYTES;
+    const uint8_t* b = stage + blk * BYTES;  // 2-byte aligned
     const float d = (float)__builtin_bit_cast(_Float16, *(const uint16_t*)b);
-    float v[32];
-    if constexpr (BYTES == 34) {
+    float v[8];
+    if constexpr (BYTES == 34) {  // values 8 part .. 8 part + 7: bytes 2 + 8 part ..
+        const uint16_t* q = (const uint16_t*)(b + 2 + 8 * part);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = d * (float)(int8_t)b[2 + i];
-    } else {
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = q[j];
+            v[2 * j] = d * (float)(int8_t)(w & 0xff);
+            v[2 * j + 1] = d * (float)(int8_t)(w >> 8);
+        }
+    } else {  // values 0-15: low nibbles of bytes 0-15; values 16-31: high nibbles
+        const uint16_t* q = (const uint16_t*)(b + 2 + 8 * (part & 1));
+        const int sh = (part >> 1) * 4;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int x = b[2 + j];
-            v[j] = d * (float)((x & 15) - 8);
-            v[j + 16] = d * (float)((x >> 4) - 8);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w = q[j];
+            v[2 * j] = d * (float)((int)((w >> sh) & 15) - 8);
+            v[2 * j + 1] = d * (float)((int)((w >> (8 + sh)) & 15) - 8);
         }
     }
-    uint16_t* o = dst + (blk0 + tid) * 32;
-#pragma unroll
-    for (int i = 0; i < 32; i += 8) {
-        const u32x4 w = {pack_op2<true>(v[i], v[i + 1]), pack_op2<true>(v[i + 2], v[i + 3]),
-                         pack_op2<true>(v[i + 4], v[i + 5]), pack_op2<true>(v[i + 6], v[i + 7])};
-        *(u32x4*)(o + i) = w;
-    }
+    const u32x4 w = {pack_op2<true>(v[0], v[1]), pack_op2<true>(v[2], v[3]), pack_op2<true>(v[4], v[5]),
+                     pack_op2<true>(v[6], v[7])};
+    *(u32x4*)(dst + (blk0 + blk) * 32 + 8 * part) = w;
 }
 
 }  // namespace

@@ -245,8 +245,8 @@ typedef enum attn_qfmt {
  * call the attention entry points with kv_dtype = ATTN_F16). d * q is exact in
  * fp32 and rounded once to fp16 (nearest even). src and dst are device
  * buffers, 16-byte aligned, not overlapping; n_blocks = 0 does nothing.
- * One thread expands one block: n_blocks above 2^32 - 256 (a grid of 2^32
- * threads) gives ATTN_ERR_UNSUPPORTED.
+ * Four threads expand one block (8 values each): n_blocks above 2^30 - 64 (a
+ * grid of 2^32 threads) gives ATTN_ERR_UNSUPPORTED.
  */
 attn_status attn_dequant_fp16(const void* src, int fmt, void* dst, int64_t n_blocks, void* stream);
 

@@ -178,7 +178,7 @@ def test_workspace_bytes():
     (0, None, FAKE, 4, 1),
     (1, ctypes.c_void_p(0x10002), FAKE, 4, 1),                # misaligned source
     (0, FAKE, FAKE, 0, 0),                                    # nothing to do (no launch)
-    (0, FAKE, FAKE, (1 << 32) - 255, 2),                      # one thread per block: grid past 2^32 threads
+    (0, FAKE, FAKE, (1 << 30) - 63, 2),                       # four threads per block: grid past 2^32 threads
 ])
 def test_dequant_rejects(fmt, src, dst, n, status):
     lib = binding.load_library()
