@@ -39,7 +39,18 @@ __global__ __launch_bounds__(64) void absorb_kernel(const uint16_t* __restrict__
                                                     uint16_t* __restrict__ u, int T, int H, int R, int DV, int t0) {
     const int lane = threadIdx.x, r16 = lane & 15, kg = lane >> 4;
     const int nvb = DV / 16;
-    const int h = blockIdx.x / nvb, vb = blockIdx.x % nvb;
+    // workgroup -> (head, block of 16 values). With H a multiple of 8, XCD x (= blockIdx % 8)
+    // takes heads x, x + 8, ...: the nvb workgroups of a head share one L2, which then serves
+    // the head's latent rows to all of them (a head-major order would fetch them on every XCD).
+    int h, vb;
+    if ((H & 7) == 0) {
+        const int j = blockIdx.x >> 3;
+        h = (blockIdx.x & 7) + 8 * (j / nvb);
+        vb = j % nvb;
+    } else {
+        h = blockIdx.x / nvb;
+        vb = blockIdx.x % nvb;
+    }
     const int nt = min(T - t0, RB * 16);
     // B operand: w_abs[h][v = vb*16 + r16][c], 8 consecutive c per lane
     const uint16_t* wrow = wa + ((size_t)h * DV + vb * 16 + r16) * R + kg * 8;
