@@ -349,10 +349,13 @@ void decode_gathered_kernel(GatherParams p) {
             }
             mx = halfwave_max(mx);
             const bool upd = mx > m_run + kTauG;
-            if (__builtin_amdgcn_ballot_w64(upd)) {
-                const float alpha = upd ? exp2_fast(m_run - mx) : 1.f;  // 0 when m_run = -inf
-                m_run = upd ? mx : m_run;
-                l_run *= alpha;
+            const float alpha = upd ? exp2_fast(m_run - mx) : 1.f;  // 0 when m_run = -inf
+            // the output of a lane whose reference was still -inf is zero: it needs no rescale
+            // (without this test the first step of every wave rescaled all 256 accumulators)
+            const bool rescale = __builtin_amdgcn_ballot_w64(upd && m_run != -INFINITY) != 0;
+            m_run = upd ? mx : m_run;
+            l_run *= alpha;
+            if (rescale) {
 #pragma unroll
                 for (int d = 0; d < DB; ++d) {  // one block at a time
                     asm volatile("" : "+a"(oacc[d]));
