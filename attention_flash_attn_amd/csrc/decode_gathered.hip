@@ -304,13 +304,13 @@ void decode_gathered_kernel(GatherParams p) {
             const char* vt = VK ? kt : kt + SSTAGE;
             const int r0 = i * 32;
 
-            // S^T = K Q^T over the 36 k-steps, K fragments read PFK steps ahead. The score
-            // accumulator lives in ordinary registers (in accumulation registers it displaced an
-            // output block, copied out and back every step).
+            // S^T = K Q^T over the 36 k-steps, K fragments read PFK steps ahead. The MFMAs write
+            // the accumulation registers, so the chain borrows one output block's (the compiler
+            // parks that block in ordinary registers meanwhile); the first MFMA takes a literal
+            // zero, and the scores move to ordinary registers once, for the softmax.
             constexpr int PFK = KK < ATTN_G_PFK ? KK : ATTN_G_PFK;
             auto kload = [&](int kk) -> bf16x8 { return *(const bf16x8*)(kt + kb[kk & 3] + (kk >> 2) * 128); };
-            f32x16 sacc = f32x16{};
-            asm volatile("" : "+v"(sacc));
+            f32x16 sacc;
             bf16x8 kring[PFK];
 #pragma unroll
             for (int j = 0; j < PFK; ++j) kring[j] = kload(j);
@@ -318,7 +318,7 @@ void decode_gathered_kernel(GatherParams p) {
             for (int kk = 0; kk < KK; ++kk) {
                 const bf16x8 a = kring[kk % PFK];
                 if (kk + PFK < KK) kring[kk % PFK] = kload(kk + PFK);
-                sacc = mma32<F16>(a, qf[kk], sacc);
+                sacc = mma32<F16>(a, qf[kk], kk == 0 ? f32x16{} : sacc);
                 __builtin_amdgcn_sched_barrier(0);
             }
             asm volatile("" : "+v"(sacc));

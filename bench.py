@@ -47,7 +47,7 @@ MEASURED_TRAFFIC = {
     "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 1342360688},
     "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 352532114},
     "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "a4b7fecdad4f8f3d", "bytes": 5035218778},
-    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "73065ce630dbf682", "bytes": 75703222},
+    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "a746c42ea46de384", "bytes": 75639656},
 }
 
 
