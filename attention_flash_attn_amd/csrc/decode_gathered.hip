@@ -35,11 +35,16 @@
 //
 // Rows are gathered 32 per step into four LDS stages (two steps computed while
 // the next two are in flight) by direct HBM -> LDS copies, 1 KB per wave
-// instruction. Stage rows sit at the row pitch (1152 bytes, 128 mod 256) with
-// 16-byte chunk c of row r stored at c ^ f(r), f(r) = bit1(r) << 2 | bit2(r) << 1,
-// which keeps both fragment reads free of bank conflicts:
-//   K operand:   a 128-bit read by 32 consecutive rows x 2 adjacent chunks
-//                (the LDS serves lanes 0-7 with 32-39, rows 8m..8m+7);
+// instruction. A stage is nine 4 KB blocks, block b holding 16-byte chunks
+// 8b..8b+7 of the 32 rows at a 128-byte pitch: chunk c of row r sits at
+// (c / 8) * 4096 + 128 r + 16 ((c % 8) ^ f(r)),
+// f(r) = bit1(r) << 2 | (bit2(r) ^ bit3(r)) << 1 | bit3(r).
+// Lane l of wave w copies row 8w + l/8 (its stored chunk l % 8 of every block), so
+// a copy instruction fills 8 rows of one block and a lane looks up one row
+// offset per step. The swizzle keeps both fragment reads free of bank conflicts:
+//   K operand:   a 128-bit read by 32 consecutive rows x 2 adjacent chunks: any
+//                16 consecutive rows at one chunk cover all 64 banks (with only
+//                bits 1 and 2 of the row in f, rows r and r + 8 collided);
 //   V^T operand: a transposing 64-bit read of 4 aligned rows x 4 chunks by 32
 //                consecutive lanes.
 // Each workgroup writes its range's output normalised by its own sum, rounded to
@@ -76,7 +81,19 @@ struct GatherParams {
 };
 
 // chunk swizzle of stage row r (see the file comment)
-__device__ __forceinline__ int gsw(int r) { return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1); }
+__device__ __forceinline__ int gsw(int r) {
+    return (((r >> 1) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 1) | ((r >> 3) & 1);
+}
+
+// Direct HBM -> LDS copy of 16 bytes per lane (lane i writes lds + 16 i), written in assembly
+// so that the compiler does not track it: tracked, it made the compiler wait for every copy in
+// flight before some LDS reads of the stages being computed. The kernel orders each copy before
+// the reads of its stage itself (a wait for the wave's copies, then a barrier). No output
+// registers; M0 carries the LDS address.
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(m) : "m0");
+}
 
 #ifndef ATTN_G_PFK
 #define ATTN_G_PFK 4  // K fragments read ahead of their MFMA
@@ -92,22 +109,25 @@ void decode_gathered_kernel(GatherParams p) {
     constexpr int KK = DK / 16;         // QK k-steps of 16
     constexpr int DB = DV / 32;         // 32-column blocks of O^T
     constexpr int DH = DB / 2;          // blocks each wave of a pair merges and stores
-    constexpr int PITCH = DK * 2;       // LDS row pitch (bytes), key and value stages alike
-    constexpr int NCH = DK / 8;         // 16-byte chunks per row
-    constexpr int SSTAGE = 32 * PITCH;  // one stage of 32 rows
-    constexpr int NSEG = SSTAGE / 1024; // 1 KB direct loads per stage
+    constexpr int NCH = DK / 8;         // 16-byte chunks per key row
+    constexpr int KBLK = NCH / 8;       // 4 KB blocks per key stage (8 chunks x 32 rows each)
+    constexpr int VBLK = DV / 64;       // blocks holding the value columns
+    constexpr int SSTAGE = KBLK * 4096; // one stage of 32 rows
     constexpr int STAGE = SSTAGE * (VK ? 1 : 2);
     constexpr int NST = VK ? 4 : 2;     // stages: two steps computed, (VK) two more in flight
-    constexpr int JW = NSEG / NW;       // copies per wave per stage (key rows)
-    static_assert(DK % 32 == 0 && DV % 64 == 0 && DV <= DK && PITCH % 256 == 128, "shape");
-    static_assert(SSTAGE % 1024 == 0 && NSEG % NW == 0 && NCH % 8 == 0, "stage");
-    static_assert(NST * STAGE + 12 * kGatherMaxSplit <= 160 * 1024, "LDS");
+    constexpr int IPT = (kGatherMaxSplit + NT - 1) / NT;  // table entries per thread
+    static_assert(DK % 64 == 0 && DV % 64 == 0 && DV <= DK && NW * 8 == 32, "shape");
+    static_assert(NST * STAGE + 12 * kGatherMaxSplit + 4 * IPT * NT / 32 <= 160 * 1024, "LDS");
     static_assert(NW * DH * 64 * 64 + NW * 64 * 8 <= NST * STAGE, "pair exchange fits the stages");
     __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
     __shared__ long long skoff[kGatherMaxSplit];  // element offset of each key row from kc
+    // key positions, +inf past the range's keys, -inf for every live key when not causal: a
+    // key is live iff its entry is <= the token's position
     __shared__ __attribute__((aligned(16))) float spos[kGatherMaxSplit];
+    __shared__ int slive[IPT * NT / 32];  // per 32-key step: all of its keys are live
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, col = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, col = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: copy destinations in SALU
     const int pair = wave & 1, par = wave >> 1;  // head half of the group; parity of the steps taken
     // workgroup -> (token, head group, key range). With xcd set, token t's workgroups run on
     // XCD t % 8 (workgroup id % 8), whose L2 then serves its queries and shared rows.
@@ -130,73 +150,56 @@ void decode_gathered_kernel(GatherParams p) {
     const int nk = nsel + has_cur;
     const float qpos = (float)p.q_pos[t];
 
-    // this range's row indices and positions (every load issued before the first LDS write)
-    constexpr int IPT = (kGatherMaxSplit + NT - 1) / NT;
+    // this range's row offsets and key positions (every load issued before the first LDS write)
     long long roff_r[IPT];
     float pos_r[IPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
         const int i = tid + u * NT;
         roff_r[u] = 0;
-        pos_r[u] = 0.f;
+        pos_r[u] = INFINITY;
         if (i < nsel) {
             roff_r[u] = (long long)p.row_index[(size_t)t * p.n_sel + start + i];
-            if (CAUSAL) pos_r[u] = p.key_pos[(size_t)t * p.n_sel + start + i];
+            pos_r[u] = CAUSAL ? p.key_pos[(size_t)t * p.n_sel + start + i] : -INFINITY;
+        } else if (i == nsel && has_cur) {
+            pos_r[u] = CAUSAL ? qpos : -INFINITY;
         }
     }
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
         const int i = tid + u * NT;
-        if (i < nsel) {
-            skoff[i] = roff_r[u] * p.row_stride;
-            spos[i] = pos_r[u];
+        if (i < nsel) skoff[i] = roff_r[u] * p.row_stride;
+        if (i < kGatherMaxSplit) spos[i] = pos_r[u];
+        // step (i / 32) is the lane's half of this wave: it needs no masking when every key is live
+        const uint64_t b = __builtin_amdgcn_ballot_w64(pos_r[u] <= qpos);
+        if (lane == 0) {
+            const int s0 = (u * NT + wave * 64) >> 5;
+            slive[s0] = (uint32_t)b == 0xffffffffu;
+            slive[s0 + 1] = (uint32_t)(b >> 32) == 0xffffffffu;
         }
     }
-    if (has_cur && tid == 0) {
-        skoff[nsel] = p.kcur_off + (long long)t * p.row_stride;
-        spos[nsel] = qpos;
-    }
+    if (has_cur && tid == 0) skoff[nsel] = p.kcur_off + (long long)t * p.row_stride;
     __syncthreads();
 
-    // Rows of step i into stage st: wave w fills 1 KB segments w, w+NW, ... All row offsets
-    // of the step are read from LDS before the first copy is issued (a copy writes LDS, so a
-    // later table read could not be moved ahead of it). Rows past the range repeat its last
-    // row, so every copy reads valid memory.
+    // Rows of step i into stage st: lane l of wave w copies row 8w + l/8 of the step, its
+    // stored chunk l % 8 of every block (logical chunk 8b + ((l % 8) ^ f(row)) of block b), so
+    // copy b of the wave writes bytes [1024 w, 1024 w + 1024) of block b. Rows past the range
+    // repeat its last row, so every copy reads valid memory. Value rows (a separate array)
+    // fill the blocks of a second stage the same way.
+    const int crow = wave * 8 + (lane >> 3);
+    const int cchunk = ((lane & 7) ^ gsw(crow)) * 8;  // element offset within a 64-element block
     auto issue = [&](int i, int st) {
-        char* sb = smem + st * STAGE;
+        char* sb = smem + st * STAGE + wave * 1024;
+        const int kr = min(i * 32 + crow, nk - 1);
+        const long long ro = skoff[kr];
+        const uint16_t* src = p.kc + ro + cchunk;
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b) dma16(src + b * 64, sb + b * 4096);
         if constexpr (!VK) {
-            // separate value rows: twice the copies; issued one row at a time, which keeps the
-            // register peak low (all offsets first made this variant spill)
-#pragma unroll 1
-            for (int j = 0; j < JW; ++j) {
-                const int sg = wave + j * NW;
-                const int off = sg * 1024 + lane * 16;
-                const int rr = off / PITCH;
-                const int kr1 = min(i * 32 + rr, nk - 1);
-                const long long ro1 = skoff[kr1];
-                const int c = ((off - rr * PITCH) >> 4) ^ gsw(rr);
-                load_lds16(p.kc + ro1 + c * 8, sb + sg * 1024);
-                // value rows use the same layout; chunks past the value width repeat earlier ones
-                const long long vo = ro1 + ((has_cur && kr1 == nsel) ? p.vcur_off - p.kcur_off : 0);
-                load_lds16(p.vc + vo + (c % (DV / 8)) * 8, sb + SSTAGE + sg * 1024);
-            }
-            return;
-        }
-        long long ro[JW];
-        int kr[JW];
+            const long long vo = ro + ((has_cur && kr == nsel) ? p.vcur_off - p.kcur_off : 0);
+            const uint16_t* vsrc = p.vc + vo + cchunk;
 #pragma unroll
-        for (int j = 0; j < JW; ++j) {
-            const int rr = ((wave + j * NW) * 1024 + lane * 16) / PITCH;
-            kr[j] = min(i * 32 + rr, nk - 1);
-            ro[j] = skoff[kr[j]];
-        }
-#pragma unroll
-        for (int j = 0; j < JW; ++j) {
-            const int sg = wave + j * NW;
-            const int off = sg * 1024 + lane * 16;
-            const int rr = off / PITCH;
-            const int c = ((off - rr * PITCH) >> 4) ^ gsw(rr);
-            load_lds16(p.kc + ro[j] + c * 8, sb + sg * 1024);
+            for (int b = 0; b < VBLK; ++b) dma16(vsrc + b * 64, sb + SSTAGE + b * 4096);
         }
     };
     const int nsteps = (nk + 31) / 32;
@@ -206,14 +209,11 @@ void decode_gathered_kernel(GatherParams p) {
     }
 
     // per-lane LDS byte offsets within a stage (also used for the query rows below).
-    // K operand of k-step kk: row col, logical chunk 2kk + hl, stored at (2kk + hl) ^ f(col)
-    //   = 2 (kk ^ g) + hl with g = f(col) / 2; for kk = 4m + n that is kb[n] + 128 m.
+    // K operand of k-step kk = 4m + n: row col, logical chunk 2kk + hl = 8m + 2n + hl, in
+    // block m at stored chunk (2n + hl) ^ f(col): kb[n] + 4096 m.
     int kb[4];
-    {
-        const int g = gsw(col) >> 1;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) kb[n] = col * PITCH + ((n ^ g) << 5) + (hl << 4);
-    }
+    for (int n = 0; n < 4; ++n) kb[n] = col * 128 + (((2 * n + hl) ^ gsw(col)) << 4);
 
     // query fragments: head col of this pair's 32, dims kk*16 + hl*8 .. +7 (the B operand of
     // S^T = K Q^T). When Q already has the operand type, the group's 64 query rows (contiguous
@@ -226,24 +226,21 @@ void decode_gathered_kernel(GatherParams p) {
     bf16x8 qf[KK];
     const bool q_lds = VK && p.q_type == (F16 ? 2 : 0);
     if (q_lds) {
-        static_assert(64 * PITCH <= 2 * STAGE, "query rows fit two stages");
+        // pair s's 32 query rows go to stage 2 + s, laid out like key rows
         char* qs = smem + 2 * STAGE;
         const uint16_t* qg = (const uint16_t*)p.q + ((size_t)t * p.Hq + hg * 64) * DK;
         const int qlast = min(64, p.Hq - hg * 64) - 1;  // rows past Hq repeat the last head
-        constexpr int QSEG = 64 * PITCH / 1024;
 #pragma unroll
-        for (int j = 0; j < QSEG / NW; ++j) {
-            const int sg = wave + j * NW;
-            const int off = sg * 1024 + lane * 16;
-            const int rr = off / PITCH;
-            const int c = ((off - rr * PITCH) >> 4) ^ gsw(rr);
-            load_lds16(qg + (size_t)min(rr, qlast) * DK + c * 8, qs + sg * 1024);
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const uint16_t* src = qg + (size_t)min(32 * s2 + crow, qlast) * DK + cchunk;
+#pragma unroll
+            for (int b = 0; b < KBLK; ++b) dma16(src + b * 64, qs + s2 * STAGE + wave * 1024 + b * 4096);
         }
         wait_vmem();
         __syncthreads();
-        const char* qw = qs + pair * 32 * PITCH;
+        const char* qw = qs + pair * STAGE;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8*)(qw + kb[kk & 3] + (kk >> 2) * 128);
+        for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8*)(qw + kb[kk & 3] + (kk >> 2) * 4096);
     } else {
         const size_t qrow = ((size_t)t * p.Hq + (hok ? h : 0)) * DK;
 #pragma unroll
@@ -255,16 +252,20 @@ void decode_gathered_kernel(GatherParams p) {
 
     // V^T operand of column block d, key half jj: two transposing reads of rows
     // 16 jj + 8 s + 4 hl + q (s = 0, 1; q = (lane & 15) / 4), columns d*32 + 16 bit4(lane) +
-    // 4 (lane & 3) .. +3, i.e. logical chunk 4d + x with x = 2 bit4(lane) + bit1(lane).
-    // f of those rows is a << 2 | hl << 1 (a = bit1(q)), so the chunk is stored at
-    // 4 (d ^ a) + (x ^ 2 hl): vb[d & 1] + 128 (d >> 1) + (16 jj + 8 s) * PITCH.
-    int vb[2];
+    // 4 (lane & 3) .. +3, i.e. logical chunk 4d + x with x = 2 bit4(lane) + bit1(lane): block
+    // d >> 1, chunk 4 (d & 1) + x. f of those rows does not depend on jj, so the chunk is at
+    // vb[d & 1][s] + 4096 (d >> 1) + 16 jj * 128.
+    int vb[2][2];
     {
-        const int q4 = (lane & 15) >> 2, a = (q4 >> 1) & 1;
+        const int q4 = (lane & 15) >> 2;
         const int x = (((lane >> 4) & 1) << 1) | ((lane >> 1) & 1);
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-            vb[b] = (4 * hl + q4) * PITCH + ((b ^ a) << 6) + ((x ^ (hl << 1)) << 4) + ((lane & 1) << 3);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int row = 8 * s2 + 4 * hl + q4;
+                vb[b][s2] = row * 128 + (((4 * b + x) ^ gsw(row)) << 4) + ((lane & 1) << 3);
+            }
     }
 
     // The 16 output blocks stay in the accumulation registers for the whole loop: the empty
@@ -309,7 +310,7 @@ void decode_gathered_kernel(GatherParams p) {
             // parks that block in ordinary registers meanwhile); the first MFMA takes a literal
             // zero, and the scores move to ordinary registers once, for the softmax.
             constexpr int PFK = KK < ATTN_G_PFK ? KK : ATTN_G_PFK;
-            auto kload = [&](int kk) -> bf16x8 { return *(const bf16x8*)(kt + kb[kk & 3] + (kk >> 2) * 128); };
+            auto kload = [&](int kk) -> bf16x8 { return *(const bf16x8*)(kt + kb[kk & 3] + (kk >> 2) * 4096); };
             f32x16 sacc;
             bf16x8 kring[PFK];
 #pragma unroll
@@ -323,31 +324,30 @@ void decode_gathered_kernel(GatherParams p) {
             }
             asm volatile("" : "+v"(sacc));
 
-            // scores (log2 units), masks, per-head maximum: lane value i3 is key
-            // r0 + 8 (i3 / 4) + 4 hl + i3 % 4 of head col
-            f32x4 kpos[4];
-            if constexpr (CAUSAL) {
+            // masks and per-head maximum: lane value i3 is key r0 + 8 (i3 / 4) + 4 hl + i3 % 4 of
+            // head col. Softcapped scores are transformed first (log2 units); plain ones stay raw
+            // (the scale is positive, so the raw maximum gives the scaled one, and the scale
+            // joins the exponent's fused multiply-add).
+            if constexpr (SOFTCAP) {
+#pragma unroll
+                for (int i3 = 0; i3 < 16; ++i3) {
+                    const float ex = exp2_fast(sacc[i3] * p.c_tanh);
+                    sacc[i3] = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(ex + 1.f);
+                }
+            }
+            if (!__builtin_amdgcn_readfirstlane(slive[i])) {
+                f32x4 kpos[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) kpos[j] = *(const f32x4*)(spos + r0 + 8 * j + 4 * hl);
+#pragma unroll
+                for (int i3 = 0; i3 < 16; ++i3)
+                    if (!(kpos[i3 >> 2][i3 & 3] <= qpos)) sacc[i3] = -INFINITY;
             }
             float mx = -INFINITY;
 #pragma unroll
-            for (int i3 = 0; i3 < 16; ++i3) {
-                float x = sacc[i3];
-                if constexpr (SOFTCAP) {
-                    const float ex = exp2_fast(x * p.c_tanh);
-                    x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(ex + 1.f);
-                } else {
-                    x *= p.c_score;
-                }
-                const int kl = r0 + 8 * (i3 >> 2) + 4 * hl + (i3 & 3);
-                bool live = kl < nk;
-                if constexpr (CAUSAL) live = live && kpos[i3 >> 2][i3 & 3] <= qpos;
-                if (!live) x = -INFINITY;
-                sacc[i3] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int i3 = 0; i3 < 16; ++i3) mx = fmaxf(mx, sacc[i3]);
             mx = halfwave_max(mx);
+            if constexpr (!SOFTCAP) mx *= p.c_score;  // -inf stays -inf
             const bool upd = mx > m_run + kTauG;
             const float alpha = upd ? exp2_fast(m_run - mx) : 1.f;  // 0 when m_run = -inf
             // the output of a lane whose reference was still -inf is zero: it needs no rescale
@@ -368,7 +368,9 @@ void decode_gathered_kernel(GatherParams p) {
             uint32_t pk[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                pk[j] = pack_op2<F16>(exp2_fast(sacc[2 * j] + nm), exp2_fast(sacc[2 * j + 1] + nm));
+                const float x0 = SOFTCAP ? sacc[2 * j] + nm : fmaf(sacc[2 * j], p.c_score, nm);
+                const float x1 = SOFTCAP ? sacc[2 * j + 1] + nm : fmaf(sacc[2 * j + 1], p.c_score, nm);
+                pk[j] = pack_op2<F16>(exp2_fast(x0), exp2_fast(x1));
                 l_run = add_op2<F16>(pk[j], l_run);
             }
 
@@ -378,9 +380,9 @@ void decode_gathered_kernel(GatherParams p) {
             const ATTN_LDS char* vtl = (const ATTN_LDS char*)vt;
             auto vload = [&](int idx) -> bf16x8 {
                 const int jj = idx / DB, d = idx % DB;
-                const ATTN_LDS char* pa = vtl + vb[d & 1] + (d >> 1) * 128 + (16 * jj) * PITCH;
-                const bf16x4 va = lds_read_tr16_l(pa);
-                const bf16x4 vv = lds_read_tr16_l(pa + 8 * PITCH);
+                const int o = (d >> 1) * 4096 + (16 * jj) * 128;
+                const bf16x4 va = lds_read_tr16_l(vtl + vb[d & 1][0] + o);
+                const bf16x4 vv = lds_read_tr16_l(vtl + vb[d & 1][1] + o);
                 return __builtin_shufflevector(va, vv, 0, 1, 2, 3, 4, 5, 6, 7);
             };
             bf16x8 vring[PFV];
@@ -467,29 +469,40 @@ void decode_gathered_kernel(GatherParams p) {
     else
         keep(std::integral_constant<int, 0>{});
     __syncthreads();  // every wave has read its partner's blocks: the exchange area is free
-    // staging [pair][32 heads][DV] bf16 (a 16-byte pad per row), then whole 1 KB rows out
+    // staging [pair][32 heads][DV] bf16 (a 16-byte pad per row), then whole 1 KB rows out.
+    // Rows 16-31 hold the two 8-byte halves of every 16-byte chunk swapped: then the 8-byte
+    // writes of rows r and r + 16 (1040 bytes apart per row) fall in different banks.
     constexpr int OPITCH = DV * 2 + 16;
     static_assert(2 * 32 * OPITCH <= NST * STAGE, "output staging fits the stages");
     char* ost = smem + pair * 32 * OPITCH;
     const int keep0 = par ? DH : 0;
+    char* ow = ost + col * OPITCH + 8 * (hl ^ (col >> 4));
 #pragma unroll
     for (int d = 0; d < DH; ++d)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            *(u32x2*)(ost + col * OPITCH + ((keep0 + d) * 32 + 8 * c + 4 * hl) * 2) = outp[d][c];
+        for (int c = 0; c < 4; ++c) *(u32x2*)(ow + ((keep0 + d) * 32 + 8 * c) * 2) = outp[d][c];
     __syncthreads();
-    // each wave stores 16 of its pair's 32 head rows, 1 KB per instruction
+    // each wave stores 16 of its pair's 32 head rows (the odd-step wave rows 16-31, which it
+    // swaps back), 1 KB per instruction
     constexpr int PER = DV * 2 / 1024;
+    auto store_rows = [&](auto sw) {
+        constexpr bool SW = decltype(sw)::value;
 #pragma unroll 4
-    for (int k = 0; k < 16 * PER; ++k) {
-        const int hh = par * 16 + k / PER, part = k % PER;
-        const int head = hg * 64 + pair * 32 + hh;
-        if (head < p.Hq) {
-            const size_t slot = ((size_t)t * p.Hq + head) * p.n_split + split;
-            *(u32x4*)((char*)p.ws_o + slot * (DV * 2) + part * 1024 + lane * 16) =
-                *(const u32x4*)(ost + hh * OPITCH + part * 1024 + lane * 16);
+        for (int k = 0; k < 16 * PER; ++k) {
+            const int hh = (SW ? 16 : 0) + k / PER, part = k % PER;
+            const int head = hg * 64 + pair * 32 + hh;
+            if (head < p.Hq) {
+                const size_t slot = ((size_t)t * p.Hq + head) * p.n_split + split;
+                const u32x4 v = *(const u32x4*)(ost + hh * OPITCH + part * 1024 + lane * 16);
+                *(u32x4*)((char*)p.ws_o + slot * (DV * 2) + part * 1024 + lane * 16) =
+                    SW ? u32x4{v[2], v[3], v[0], v[1]} : v;
+            }
         }
-    }
+    };
+    if (par)
+        store_rows(std::true_type{});
+    else
+        store_rows(std::false_type{});
 }
 
 template <bool VK, bool F16, bool CAUSAL, bool SOFTCAP>
