@@ -103,6 +103,13 @@ void decode_paged_split_kernel(SplitParams p) {
         }
         lim[cb] = min(end - 1, p.causal ? L - p.Sq + si : L - 1);  // last key this column may see
     }
+    // the smallest limit of the wave: a step ending at or before it needs no masking
+    int lim_lo = lim[0];
+#pragma unroll
+    for (int cb = 1; cb < CB; ++cb) lim_lo = min(lim_lo, lim[cb]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lim_lo = min(lim_lo, __shfl_xor(lim_lo, off));
+    lim_lo = __builtin_amdgcn_readfirstlane(lim_lo);
 
     // A 32-key step (32-aligned) lies in at most two cache blocks; their table
     // entries are read with wave-uniform (scalar) loads so that only K and V
@@ -143,7 +150,7 @@ void decode_paged_split_kernel(SplitParams p) {
 #pragma unroll
                 for (int kk = 0; kk < KQ; ++kk) {
                     const int dk0 = kk * 32 + grp * 8;
-                    if (dk0 < DK)
+                    if (DKP == DK || dk0 < DK)  // always true unless DK < 32
                         kr[kb][kk] = *(const u32x4*)(base + (size_t)(ro + (uint32_t)(dk0 * 2)));
                     else
                         kr[kb][kk] = u32x4{0, 0, 0, 0};
@@ -153,7 +160,7 @@ void decode_paged_split_kernel(SplitParams p) {
 #pragma unroll
                 for (int kk = 0; kk < KQ; ++kk) {
                     const int dk0 = kk * 32 + grp * 8;
-                    if (dk0 < DK)
+                    if (DKP == DK || dk0 < DK)  // always true unless DK < 32
                         kr[kb][kk] = *(const u32x4*)(r + dk0);
                     else
                         kr[kb][kk] = u32x4{0, 0, 0, 0};
@@ -207,8 +214,13 @@ void decode_paged_split_kernel(SplitParams p) {
             vf[d] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
+    // Softcapped scores are transformed to log2 units before the mask (one uniform branch);
+    // otherwise the raw product is masked and maximised, and the positive scale cs joins the
+    // exponent's fused multiply-add (cs = 1 for softcapped scores). A step ending at or before
+    // lim_lo is visible to every column and skips the mask.
+    const float cs = p.softcap_on ? 1.f : p.c_score;
     auto compute = [&](int k0, const u32x4 (&kc_)[2][KQ], const bf16x8 (&vf)[DBV]) {
-
+        const bool full = k0 + 31 <= lim_lo;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             // S^T for 32 keys: two 16-key blocks
@@ -220,24 +232,29 @@ void decode_paged_split_kernel(SplitParams p) {
                 for (int kk = 0; kk < KQ; ++kk)
                     sacc[kb] = mma16<F16>(__builtin_bit_cast(bf16x8, kc_[kb][kk]), qf[cb][kk], sacc[kb]);
             }
+            if (p.softcap_on) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = exp2_fast(sacc[kb][i] * p.c_tanh);
+                        sacc[kb][i] = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
+                    }
+            }
+            if (!full) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (k0 + kb * 16 + grp * 4 + i > lim[cb]) sacc[kb][i] = -INFINITY;
+            }
             float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x = sacc[kb][i];
-                    if (p.softcap_on) {
-                        const float e = exp2_fast(x * p.c_tanh);
-                        x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
-                    } else {
-                        x *= p.c_score;
-                    }
-                    if (k0 + kb * 16 + grp * 4 + i > lim[cb]) x = -INFINITY;
-                    sacc[kb][i] = x;
-                    mx = fmaxf(mx, x);
-                }
-            }
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
             mx = quarterwave_max(mx);
+            mx *= cs;  // -inf stays -inf
             const bool upd = mx > m_run[cb] + kTau;
             if (__builtin_amdgcn_ballot_w64(upd)) {
                 const float alpha = upd ? exp2_fast(m_run[cb] - mx) : 1.f;
@@ -251,8 +268,12 @@ void decode_paged_split_kernel(SplitParams p) {
             uint32_t pk[4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                pk[2 * kb] = pack_op2<F16>(exp2_fast(sacc[kb][0] + nm), exp2_fast(sacc[kb][1] + nm));
-                pk[2 * kb + 1] = pack_op2<F16>(exp2_fast(sacc[kb][2] + nm), exp2_fast(sacc[kb][3] + nm));
+                float e[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    e[i] = exp2_fast(fmaf(sacc[kb][i], cs, nm));
+                pk[2 * kb] = pack_op2<F16>(e[0], e[1]);
+                pk[2 * kb + 1] = pack_op2<F16>(e[2], e[3]);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) l_run[cb] = add_op2<F16>(pk[j], l_run[cb]);
