@@ -61,6 +61,7 @@ template <int DK, int DV, int CB, bool F16>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(DK <= 128 ? 2 : 1)))
 void decode_paged_split_kernel(SplitParams p) {
     constexpr int DKP = DK < 32 ? 32 : DK;  // QK k-steps of 32 (zero-padded)
+    constexpr bool LEAN = DK <= 128;        // two waves per SIMD: the lean step below
     constexpr int KQ = DKP / 32;
     constexpr int DBV = DV / 16;            // 16-row blocks of O^T
     constexpr int NCV = DV / 8;             // 16-byte chunks per V row
@@ -150,7 +151,7 @@ void decode_paged_split_kernel(SplitParams p) {
 #pragma unroll
                 for (int kk = 0; kk < KQ; ++kk) {
                     const int dk0 = kk * 32 + grp * 8;
-                    if (DKP == DK || dk0 < DK)  // always true unless DK < 32
+                    if ((LEAN && DKP == DK) || dk0 < DK)
                         kr[kb][kk] = *(const u32x4*)(base + (size_t)(ro + (uint32_t)(dk0 * 2)));
                     else
                         kr[kb][kk] = u32x4{0, 0, 0, 0};
@@ -160,7 +161,7 @@ void decode_paged_split_kernel(SplitParams p) {
 #pragma unroll
                 for (int kk = 0; kk < KQ; ++kk) {
                     const int dk0 = kk * 32 + grp * 8;
-                    if (DKP == DK || dk0 < DK)  // always true unless DK < 32
+                    if ((LEAN && DKP == DK) || dk0 < DK)
                         kr[kb][kk] = *(const u32x4*)(r + dk0);
                     else
                         kr[kb][kk] = u32x4{0, 0, 0, 0};
@@ -214,13 +215,15 @@ void decode_paged_split_kernel(SplitParams p) {
             vf[d] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    // Softcapped scores are transformed to log2 units before the mask (one uniform branch);
-    // otherwise the raw product is masked and maximised, and the positive scale cs joins the
-    // exponent's fused multiply-add (cs = 1 for softcapped scores). A step ending at or before
-    // lim_lo is visible to every column and skips the mask.
+    // LEAN (two waves per SIMD): softcapped scores are transformed to log2 units before the
+    // mask (one uniform branch); otherwise the raw product is masked and maximised, and the
+    // positive scale cs joins the exponent's fused multiply-add (cs = 1 for softcapped scores).
+    // A step ending at or before lim_lo is visible to every column and skips the mask. The
+    // one-wave instances (head dims >= 192) keep the per-score form: the lean one measured
+    // 2.5-6% slower there.
     const float cs = p.softcap_on ? 1.f : p.c_score;
     auto compute = [&](int k0, const u32x4 (&kc_)[2][KQ], const bf16x8 (&vf)[DBV]) {
-        const bool full = k0 + 31 <= lim_lo;
+        const bool full = LEAN && k0 + 31 <= lim_lo;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             // S^T for 32 keys: two 16-key blocks
@@ -232,29 +235,48 @@ void decode_paged_split_kernel(SplitParams p) {
                 for (int kk = 0; kk < KQ; ++kk)
                     sacc[kb] = mma16<F16>(__builtin_bit_cast(bf16x8, kc_[kb][kk]), qf[cb][kk], sacc[kb]);
             }
-            if (p.softcap_on) {
+            float mx = -INFINITY;
+            if constexpr (LEAN) {
+                if (p.softcap_on) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float e = exp2_fast(sacc[kb][i] * p.c_tanh);
+                            sacc[kb][i] = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
+                        }
+                }
+                if (!full) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (k0 + kb * 16 + grp * 4 + i > lim[cb]) sacc[kb][i] = -INFINITY;
+                }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
+                mx = quarterwave_max(mx) * cs;  // -inf stays -inf
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float e = exp2_fast(sacc[kb][i] * p.c_tanh);
-                        sacc[kb][i] = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
+                        float x = sacc[kb][i];
+                        if (p.softcap_on) {
+                            const float e = exp2_fast(x * p.c_tanh);
+                            x = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(e + 1.f);
+                        } else {
+                            x *= p.c_score;
+                        }
+                        if (k0 + kb * 16 + grp * 4 + i > lim[cb]) x = -INFINITY;
+                        sacc[kb][i] = x;
+                        mx = fmaxf(mx, x);
                     }
+                }
+                mx = quarterwave_max(mx);
             }
-            if (!full) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (k0 + kb * 16 + grp * 4 + i > lim[cb]) sacc[kb][i] = -INFINITY;
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
-            mx = quarterwave_max(mx);
-            mx *= cs;  // -inf stays -inf
             const bool upd = mx > m_run[cb] + kTau;
             if (__builtin_amdgcn_ballot_w64(upd)) {
                 const float alpha = upd ? exp2_fast(m_run[cb] - mx) : 1.f;
@@ -271,7 +293,7 @@ void decode_paged_split_kernel(SplitParams p) {
                 float e[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    e[i] = exp2_fast(fmaf(sacc[kb][i], cs, nm));
+                    e[i] = exp2_fast(LEAN ? fmaf(sacc[kb][i], cs, nm) : sacc[kb][i] + nm);
                 pk[2 * kb] = pack_op2<F16>(e[0], e[1]);
                 pk[2 * kb + 1] = pack_op2<F16>(e[2], e[3]);
             }

@@ -194,6 +194,10 @@ def test_gathered_small_and_ragged():
 def test_gathered_position_mask():
     check_gathered(4, 32, 8192, 512, future=64, seed=303)             # 64 keys per token lie after it
     check_gathered(2, 32, 8192, 512, causal=False, future=64, seed=304)
+    # keys after the token scattered over every range and step (a step with all keys live skips
+    # the mask, one with any key after the token takes it)
+    check_gathered(3, 64, 8192, 700, future=200, shuffle=True, seed=308)
+    check_gathered(2, 128, 8192, 2048, future=77, shuffle=True, o_dtype="bf16", seed=309)
 
 
 def test_gathered_softcap_sinks_order_and_layout():
