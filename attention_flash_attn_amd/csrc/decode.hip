@@ -471,45 +471,54 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
 
 // Combine of the gathered mode's ranges: the partial rows are 512 bf16 columns holding O_s / l_s,
 // merged with weights l_s e^{m_s - M}. One wavefront per output row (token, head); lane i owns
-// columns 8i .. 8i+7 (one 16-byte load per range). The first 8 ranges are loaded before the
-// range maxima are read; further ranges follow 8 at a time (indices clamped, weights of
+// columns 8i .. 8i+7 (one 16-byte load per range). The first 8 ranges and their (max, sum)
+// pairs are loaded together; further ranges follow 8 at a time (indices clamped, weights of
 // missing ranges zero).
 template <bool OF32>
 __global__ __launch_bounds__(64) void decode_combine_norm_kernel(CombineParams p) {
     constexpr int DV = 512, U = 8;
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
     const int lane = threadIdx.x;
     const size_t row = blockIdx.x;
     const int h = (int)(row % p.Hq);
     const int nv = p.n_split;
+    // lane u < 8 of a batch loads the (max, sum) pair of range s0 + u with the batch's row loads
+    // (one memory latency per row); v_readlane hands the pairs to every lane
     const float* ml = p.ws_ml + row * nv * 2;
     const uint16_t* ob = (const uint16_t*)p.ws_o + row * nv * DV + lane * 8;
     u32x4 x[U];
+    f32x2_t mlv;
     auto load_batch = [&](int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) x[u] = *(const u32x4*)(ob + (size_t)min(s0 + u, nv - 1) * DV);
+        mlv = *(const f32x2_t*)(ml + 2 * min(s0 + (lane & (U - 1)), nv - 1));
     };
+    auto pair_m = [&](int u) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[0]), u)); };
+    auto pair_l = [&](int u) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[1]), u)); };
     load_batch(0);
-    float M = -INFINITY;
-    for (int s = lane; s < nv; s += 64) M = fmaxf(M, ml[2 * s]);
+    float M = -INFINITY;  // clamped repeats of the last range do not change the maximum
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    for (int u = 0; u < U; ++u) M = fmaxf(M, pair_m(u));
+    if (nv > U) {  // more than one batch: the other maxima first
+        float mx = -INFINITY;
+        for (int s = U + lane; s < nv; s += 64) mx = fmaxf(mx, ml[2 * s]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        M = fmaxf(M, mx);
+    }
     const bool has_sink = p.sinks != nullptr;
     const float sink2 = has_sink ? p.sinks[h] * kLog2e : -INFINITY;
     const float M2 = fmaxf(M, sink2);
     const float Mu = (M2 == -INFINITY) ? 0.f : M2;
     float l = 0.f;
-    for (int s = lane; s < nv; s += 64) l += ml[2 * s + 1] * exp2_fast(ml[2 * s] - Mu);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-    if (has_sink) l += exp2_fast(sink2 - Mu);
-    const float inv = l > 0.f ? 1.f / l : 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nv; s0 += U) {
         if (s0 != 0) load_batch(s0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s = min(s0 + u, nv - 1);
-            const float w = (s0 + u < nv) ? ml[2 * s + 1] * exp2_fast(ml[2 * s] - Mu) : 0.f;
+            // range s was stored divided by its own sum: weight l_s 2^(m_s - M)
+            const float w = (s0 + u < nv) ? pair_l(u) * exp2_fast(pair_m(u) - Mu) : 0.f;
+            l += w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 acc[2 * e] += w * bf16lo_to_f32(x[u][e]);
@@ -517,6 +526,8 @@ __global__ __launch_bounds__(64) void decode_combine_norm_kernel(CombineParams p
             }
         }
     }
+    if (has_sink) l += exp2_fast(sink2 - Mu);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     if constexpr (OF32) {
         float* o = (float*)p.o + row * DV + lane * 8;
         *(f32x4*)o = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
