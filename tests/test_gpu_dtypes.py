@@ -93,11 +93,15 @@ def test_paged_operand_types(qt, kvt):
     check_close(host(o), ro, "f32", "paged %s/%s" % (qt, kvt))
 
 
-def test_gathered_f16_cache_f32_query():
+@pytest.mark.parametrize("qt,kvt", [("f32", "f16"), ("f16", "f16"), ("f32", "bf16"), ("f16", "bf16")])
+def test_gathered_operand_types(qt, kvt):
+    """Queries already in the rows' type are staged through LDS like the rows; the others are
+    converted on load, one 16-byte piece per lane."""
+    print("gathered q=%s rows=%s" % (qt, kvt), flush=True)
     T, Hq, n_rows, n_sel = 4, 128, 4096, 700
     case = synth.gathered_case(430, T, Hq, 576, 512, n_rows, n_sel, row_dim=576, future_keys=32)
-    kv = synth.normal_typed(430, 1, (n_rows, 576), "f16")
-    q = synth.normal_typed(430, 0, (T, Hq, 576), "f32")
+    kv = synth.normal_typed(430, 1, (n_rows, 576), kvt)
+    q = synth.normal_typed(430, 0, (T, Hq, 576), qt)
     kvd = to_dev(kv)
     o = torch.empty((T, 1, Hq, 512), device="cuda", dtype=torch.float32)
     ws = torch.empty(binding.attn_decode_workspace_bytes(T, Hq, 1, 1, n_sel, 576, 512), device="cuda",
@@ -107,4 +111,4 @@ def test_gathered_f16_cache_f32_query():
                             key_pos=dev(case["key_pos"]), q_pos=dev(case["q_pos"]))
     torch.cuda.synchronize()
     ro, _ = oracle.decode_gathered(q, kv, kv[:, :512], case["row_index"], case["key_pos"], case["q_pos"], 1 / 24)
-    check_close(host(o[:, 0]), ro, "f32", "gathered fp16 cache, fp32 q")
+    check_close(host(o[:, 0]), ro, "f32", "gathered %s rows, %s q" % (kvt, qt))
