@@ -216,17 +216,16 @@ void decode_gathered_kernel(GatherParams p) {
     for (int n = 0; n < 4; ++n) kb[n] = col * 128 + (((2 * n + hl) ^ gsw(col)) << 4);
 
     // query fragments: head col of this pair's 32, dims kk*16 + hl*8 .. +7 (the B operand of
-    // S^T = K Q^T). When Q already has the operand type, the group's 64 query rows (contiguous
-    // in memory, 64 * DK * 2 bytes = two stages) are copied into the two stages not yet in
-    // use with whole 1 KB loads and read back like K fragments; otherwise (Q converted on
-    // load) each lane loads its 16-byte pieces.
+    // S^T = K Q^T). When Q already has the operand type, the group's 64 query rows are copied
+    // into the two stages not yet in use (pair s's 32 rows into stage 2 + s, laid out and
+    // copied like a step's key rows) and read back like K fragments; otherwise (Q converted
+    // on load) each lane loads its 16-byte pieces.
     const int h = hg * 64 + pair * 32 + col;
     const bool hok = h < p.Hq;
     const bool wave_on = hg * 64 + pair * 32 < p.Hq;  // wave-uniform: any head of this wave exists
     bf16x8 qf[KK];
     const bool q_lds = VK && p.q_type == (F16 ? 2 : 0);
     if (q_lds) {
-        // pair s's 32 query rows go to stage 2 + s, laid out like key rows
         char* qs = smem + 2 * STAGE;
         const uint16_t* qg = (const uint16_t*)p.q + ((size_t)t * p.Hq + hg * 64) * DK;
         const int qlast = min(64, p.Hq - hg * 64) - 1;  // rows past Hq repeat the last head

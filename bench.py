@@ -47,7 +47,7 @@ MEASURED_TRAFFIC = {
     "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 1342360008},
     "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 352533274},
     "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "73bbbc4bbd816162", "bytes": 5035344418},
-    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "c467ff312d97386a", "bytes": 75602727},
+    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "8c1df4273d5f6563", "bytes": 75602727},
 }
 
 
