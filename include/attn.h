@@ -86,7 +86,10 @@ const char* attn_status_string(int status);
 const char* attn_last_error(void);
 
 /*
- * Prefill (dense) attention.
+ * Prefill (dense) attention: the fa.metal tensor kernel of the "ggml-metal: FA tensor
+ * path: gate to the (256, 256) shape" page for a whole query block at once (its score
+ * step, online softmax, final "sinks, O /= S" block and GQA head map), with the scale
+ * applied to the unscaled product as on the "UMMA FMHA" page, "Key lessons learned".
  *   q     bf16 [B, Sq, Hq, dk]   contiguous
  *   k     bf16 [B, Sk, Hkv, dk]  contiguous
  *   v     bf16 [B, Sk, Hkv, dv]  contiguous
@@ -146,7 +149,13 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
 
 /*
  * Decode attention: Sq query rows per sequence (Sq = 1 is the single-token
- * case) against a KV cache read in one of two modes. The keys are split into
+ * case) against a KV cache read in one of two modes. Paged mode is the same
+ * operation as the prefill (same page and steps) over keys addressed through a
+ * block table; gathered mode follows the "MLA Decode Attention Kernel API
+ * Reference" page, Background and parameters (rows gathered from the cache by a
+ * row list in its native layout, a key live iff its position is at or before the
+ * token's, the token's own row as one more key) and its Notes (the tokens of a
+ * call batched into the matrix products). The keys are split into
  * fixed-size ranges processed in parallel, then merged by log-sum-exp. The
  * range length (paged 256..4096 keys, gathered 64..1024) depends only on the
  * sizes passed here and to attn_decode_workspace_bytes. Launch-size limits
