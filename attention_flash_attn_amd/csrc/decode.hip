@@ -490,7 +490,8 @@ __global__ __launch_bounds__(64) void decode_combine_norm_kernel(CombineParams p
     f32x2_t mlv;
     auto load_batch = [&](int s0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) x[u] = *(const u32x4*)(ob + (size_t)min(s0 + u, nv - 1) * DV);
+        for (int u = 0; u < U; ++u)
+            x[u] = __builtin_nontemporal_load((const u32x4*)(ob + (size_t)min(s0 + u, nv - 1) * DV));
         mlv = *(const f32x2_t*)(ml + 2 * min(s0 + (lane & (U - 1)), nv - 1));
     };
     auto pair_m = [&](int u) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[0]), u)); };

@@ -493,8 +493,8 @@ void decode_gathered_kernel(GatherParams p) {
             if (head < p.Hq) {
                 const size_t slot = ((size_t)t * p.Hq + head) * p.n_split + split;
                 const u32x4 v = *(const u32x4*)(ost + hh * OPITCH + part * 1024 + lane * 16);
-                *(u32x4*)((char*)p.ws_o + slot * (DV * 2) + part * 1024 + lane * 16) =
-                    SW ? u32x4{v[2], v[3], v[0], v[1]} : v;
+                __builtin_nontemporal_store(SW ? u32x4{v[2], v[3], v[0], v[1]} : v,
+                                            (u32x4*)((char*)p.ws_o + slot * (DV * 2) + part * 1024 + lane * 16));
             }
         }
     };
