@@ -94,21 +94,27 @@ def test_paged_operand_types(qt, kvt):
 
 
 @pytest.mark.parametrize("qt,kvt", [("f32", "f16"), ("f16", "f16"), ("f32", "bf16"), ("f16", "bf16")])
-def test_gathered_operand_types(qt, kvt):
+@pytest.mark.parametrize("cur", [False, True])
+def test_gathered_operand_types(qt, kvt, cur):
     """Queries already in the rows' type are staged through LDS like the rows; the others are
-    converted on load, one 16-byte piece per lane."""
-    print("gathered q=%s rows=%s" % (qt, kvt), flush=True)
+    converted on load, one 16-byte piece per lane. With and without the token's own row (one
+    more key of the last range) in the same types."""
+    print("gathered q=%s rows=%s cur=%d" % (qt, kvt, cur), flush=True)
     T, Hq, n_rows, n_sel = 4, 128, 4096, 700
     case = synth.gathered_case(430, T, Hq, 576, 512, n_rows, n_sel, row_dim=576, future_keys=32)
     kv = synth.normal_typed(430, 1, (n_rows, 576), kvt)
     q = synth.normal_typed(430, 0, (T, Hq, 576), qt)
+    kc = synth.normal_typed(430, 2, (T, 576), kvt) if cur else None
     kvd = to_dev(kv)
+    kcd = to_dev(kc) if cur else None
     o = torch.empty((T, 1, Hq, 512), device="cuda", dtype=torch.float32)
     ws = torch.empty(binding.attn_decode_workspace_bytes(T, Hq, 1, 1, n_sel, 576, 512), device="cuda",
                      dtype=torch.uint8)
     binding.attn_decode_fwd(to_dev(q).view(T, 1, Hq, 576), kvd[:, :576], kvd[:, :512], o, ws, scale=1 / 24,
                             Sk_max=n_sel, causal=True, row_index=dev(case["row_index"]),
-                            key_pos=dev(case["key_pos"]), q_pos=dev(case["q_pos"]))
+                            key_pos=dev(case["key_pos"]), q_pos=dev(case["q_pos"]),
+                            k_cur=kcd, v_cur=None if kcd is None else kcd[:, :512])
     torch.cuda.synchronize()
-    ro, _ = oracle.decode_gathered(q, kv, kv[:, :512], case["row_index"], case["key_pos"], case["q_pos"], 1 / 24)
-    check_close(host(o[:, 0]), ro, "f32", "gathered %s rows, %s q" % (kvt, qt))
+    ro, _ = oracle.decode_gathered(q, kv, kv[:, :512], case["row_index"], case["key_pos"], case["q_pos"], 1 / 24,
+                                   k_cur=kc, v_cur=None if kc is None else kc[:, :512])
+    check_close(host(o[:, 0]), ro, "f32", "gathered %s rows, %s q, cur %d" % (kvt, qt, cur))
