@@ -43,11 +43,11 @@ _D256_SRC = ("prefill.hip", "prefill_d256.hip", "attn_device.hpp", "../build.py"
 _DECODE_SRC = ("decode.hip", "attn_device.hpp", "../build.py")
 _GATHER_SRC = ("decode.hip", "decode_gathered.hip", "attn_device.hpp", "../build.py")
 MEASURED_TRAFFIC = {
-    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "bced5b9d78d0ce7a", "bytes": 604591922},
-    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 1342360008},
-    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 352533274},
-    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "73bbbc4bbd816162", "bytes": 5035344418},
-    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "8c1df4273d5f6563", "bytes": 75602727},
+    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "bced5b9d78d0ce7a", "bytes": 653886965},
+    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 1342359955},
+    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 352533876},
+    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "d0ef77d9f69752c7", "bytes": 5035347225},
+    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "86d212c61d15fced", "bytes": 75633194},
 }
 
 
