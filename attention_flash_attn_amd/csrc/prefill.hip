@@ -93,7 +93,7 @@ constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 template <int DK, int DV, int BN, int NW, int OCC, bool CAUSAL, bool SOFTCAP, bool ADDM, bool F16, bool OF32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(OCC)))
 void prefill_kernel(PrefillParams p) {
-    constexpr bool LOG2 = SOFTCAP || ADDM;  // scores converted to log2 units before the max
+    constexpr bool LOG2 = SOFTCAP;  // scores converted to log2 units before the max
     constexpr int NT = NW * 64;
     constexpr int BM = NW * 32;             // query rows per workgroup
     constexpr int DVP = DV < 32 ? 32 : DV;  // V rows padded to a whole 32-row block of O^T
@@ -231,7 +231,7 @@ void prefill_kernel(PrefillParams p) {
     // Chunk c of row r sits at slot c ^ mswz(r): a lane's 8-byte read of its row then
     // shares a bank pair with at most one other lane of its half-wave.
     i32x4 mrsrc = {0, 0, 0, 0};
-    float ms2 = 0.f;  // slope * log2 e
+    float ms2 = 0.f;  // slope * log2 e (softcap: scores in log2 units), else slope / scale (raw units)
     constexpr int MCH = BN * 2 / 16;       // 16-byte chunks per mask row of a tile
     constexpr int MRPI = 1024 / (BN * 2);  // mask rows per 1 KB copy
     auto mswz = [](int r) { return (r >> 1) & (MCH - 1); };
@@ -245,7 +245,7 @@ void prefill_kernel(PrefillParams p) {
         const float e = h < p.n_head_log2 ? -(float)(h + 1) * p.max_bias / (float)p.n_head_log2
                                           : -(float)(2 * (h - p.n_head_log2) + 1) * p.max_bias /
                                                 (2.f * (float)p.n_head_log2);
-        ms2 = exp2_fast(e) * kLog2e;
+        ms2 = exp2_fast(e) * (SOFTCAP ? kLog2e : kLog2e / p.c_score);
     }
     // mask entries of tile t into stage st (keys past the slab end are not copied; they
     // only occur in the masked last tile, where those keys are excluded)
@@ -303,7 +303,8 @@ void prefill_kernel(PrefillParams p) {
             }
         }
         if constexpr (ADDM) {
-            // log2-unit score plus slope * mask entry (fp16 -inf stays -inf)
+            // score plus slope * mask entry, in the score's units: log2 units after the softcap,
+            // else raw, the scale joining the exponent as without a mask (fp16 -inf stays -inf)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -312,8 +313,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int i = g4 * 4 + e;
-                        const float base = SOFTCAP ? sacc[kb][i] : sacc[kb][i] * p.c_score;
-                        sacc[kb][i] = __builtin_fmaf((float)mv[e], ms2, base);
+                        sacc[kb][i] = __builtin_fmaf((float)mv[e], ms2, sacc[kb][i]);
                     }
                 }
             }
