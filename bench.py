@@ -43,11 +43,11 @@ _D256_SRC = ("prefill.hip", "prefill_d256.hip", "attn_device.hpp", "../build.py"
 _DECODE_SRC = ("decode.hip", "attn_device.hpp", "../build.py")
 _GATHER_SRC = ("decode.hip", "decode_gathered.hip", "attn_device.hpp", "../build.py")
 MEASURED_TRAFFIC = {
-    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "bced5b9d78d0ce7a", "bytes": 653886965},
-    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 1342359955},
-    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "97f2a0b1344d806c", "bytes": 352533876},
-    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "d0ef77d9f69752c7", "bytes": 5035347225},
-    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "86d212c61d15fced", "bytes": 75633194},
+    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "a46d3a9fa555b0dd", "bytes": 656558729},
+    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "a1f12f5b49511733", "bytes": 1342339163},
+    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "a1f12f5b49511733", "bytes": 352547608},
+    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "d0ef77d9f69752c7", "bytes": 5035338637},
+    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "86d212c61d15fced", "bytes": 75632569},
 }
 
 
