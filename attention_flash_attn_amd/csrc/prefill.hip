@@ -290,8 +290,12 @@ void prefill_kernel(PrefillParams p) {
             sacc[idx / KK] = mma32<F16>(a, qf[idx % KK], sacc[idx / KK]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // scores in log2 units (softcap) or raw (scaled inside the exponent), mask, tile max
-        if constexpr (SOFTCAP) {
+        // scores in log2 units (softcap) or raw (scaled inside the exponent), mask, tile max.
+        // A softcapped tile with no mask of either kind takes its maximum over the raw scores
+        // (the cap is increasing, so the capped maximum is the cap of the raw one) and keeps
+        // only r = 1 / (e^{2y} + 1) per score: the exponent c_cap - 2 c_cap r - m is then one FMA.
+        constexpr bool CAPR = SOFTCAP && !ADDM && !MASK;
+        if constexpr (SOFTCAP && !CAPR) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -335,6 +339,7 @@ void prefill_kernel(PrefillParams p) {
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
         }
         mx = halfwave_max(mx);
+        if constexpr (CAPR) mx = p.c_cap - 2.f * p.c_cap * __builtin_amdgcn_rcpf(exp2_fast(mx * p.c_tanh) + 1.f);
         const float cs = LOG2 ? 1.f : p.c_score;
         const float m_tile = LOG2 ? mx : mx * cs;
         // lazy reference update: only when the tile max exceeds the reference by > 2^tau
@@ -349,14 +354,16 @@ void prefill_kernel(PrefillParams p) {
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         const float nm = -m_use;
+        const float xa = CAPR ? -2.f * p.c_cap : cs, xb = CAPR ? p.c_cap + nm : nm;  // exponent xa * s + xb
+        auto arg = [&](float x) { return CAPR ? __builtin_amdgcn_rcpf(exp2_fast(x * p.c_tanh) + 1.f) : x; };
         // P = 2^(s - m) rounded to bf16, packed as the PV operand; sum of the rounded values
         uint32_t pk[KB][8];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float p0 = exp2_fast(__builtin_fmaf(sacc[kb][2 * j], cs, nm));
-                const float p1 = exp2_fast(__builtin_fmaf(sacc[kb][2 * j + 1], cs, nm));
+                const float p0 = exp2_fast(__builtin_fmaf(arg(sacc[kb][2 * j]), xa, xb));
+                const float p1 = exp2_fast(__builtin_fmaf(arg(sacc[kb][2 * j + 1]), xa, xb));
                 pk[kb][j] = pack_op2<F16>(p0, p1);
                 l_run = add_op2<F16>(pk[kb][j], l_run);
             }
