@@ -78,7 +78,7 @@ void decode_paged_split_kernel(SplitParams p) {
     const int L = p.seq_lens[b];
     const int start = split * p.split_len;
     if (start >= L) return;  // the combine pass only reads splits that start below L
-    const int end = min(L, start + p.split_len);
+    const int end = start + min(L - start, p.split_len);
     const int bs = 1 << p.bs_log2;
     const int32_t* table = p.block_table + (size_t)b * p.max_blocks;
 
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(CombineParams p) {
     int nv = p.n_split;
     if (p.seq_lens != nullptr) {
         const int L = p.seq_lens[b];
-        nv = min(p.n_split, (L + p.split_len - 1) / p.split_len);
+        nv = min(p.n_split, L > 0 ? (L - 1) / p.split_len + 1 : 0);  // no overflow at long splits
     }
     const float* ml = p.ws_ml + row * p.n_split * 2;
     const float* ob = (const float*)p.ws_o + row * p.n_split * p.dv;
@@ -612,19 +612,32 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
         while (sl < len && sl < 1024) sl <<= 1;
         pl.split_len = sl;
     } else {
-        // paged: one wavefront per (split, KV head, sequence). Aim for about 4096 of them
-        // (two rounds of two waves per SIMD) with splits of 256..2048 (4096) keys: long splits
-        // when there are many sequences (fewer partial rows to merge), short ones when few
-        const long long pairs = (long long)B * Hkv;
-        const long long want = (4096 + pairs - 1) / pairs;  // splits per (KV head, sequence)
-        long long len = Sk_max > 0 ? (Sk_max + want - 1) / want : 256;
-        // The fp32 partials grow with the query columns per KV head, so 32-column groups
-        // (paged_cols) take splits of up to 4096 keys (4 tokens x 8 heads, 64 sequences of
-        // up to 32K keys: 984 -> 955 us; one token stays at 2048, 8192 was slower for both)
-        const int max_sl = paged_cols(dk, Sq * (Hq / Hkv)) == 32 ? 4096 : 2048;
-        int sl = 256;
-        while (sl < len && sl < max_sl) sl <<= 1;
-        pl.split_len = sl;
+        // paged: one wavefront per (split, KV head, column group, sequence), with 2048 wave
+        // slots on the chip (two waves per SIMD at head dims <= 128, else 1024). A split waits
+        // for a slot only when more splits exist than slots, and such late starters set the
+        // end of the launch, so the splits are made as short as possible while the expected
+        // number of non-empty ones still fits in 90% of the slots. The lengths are device data;
+        // taking them spread evenly up to Sk_max, n splits of a full-length sequence leave
+        // (n + 1) / 2 per sequence on average: units * (n + 1) / 2 <= 0.9 * slots. Split
+        // lengths are powers of two up to 1024 keys and multiples of 1024 above.
+        // Measured at 64 sequences of 1024..32768 keys, 8 KV heads, d = 128 (one KV-head
+        // column group), split lengths against time per call:
+        //   one token:      2048: 853-857 us, 3072: 838, 4096: 863, 5120: 922, 6144: 814
+        //   4 draft tokens: 3072: 925, 4096: 928-938, 5120: 975, 6144: 868-870, 7168: 937,
+        //                   8192: 987
+        // This rule picks 6 splits (6144 keys) there: 231 of each XCD's 256 slots.
+        const long long nq = (long long)Sq * (Hkv > 0 ? Hq / Hkv : 1);
+        const long long cols = paged_cols(dk, (int)(nq < (1 << 30) ? nq : (1 << 30)));
+        long long units = (long long)B * Hkv * ((nq + cols - 1) / cols);
+        if (units < 1) units = 1;
+        const long long slots = dk <= 128 ? 2048 : 1024;
+        long long n = (18 * slots / units - 10) / 10;  // floor(1.8 * slots / units - 1)
+        if (n < 1) n = 1;
+        const long long len = Sk_max > 0 ? (Sk_max + n - 1) / n : 256;
+        long long sl = 256;
+        while (sl < len && sl < 1024) sl <<= 1;
+        if (sl < len) sl = (len + 1023) / 1024 * 1024;
+        pl.split_len = (int)(sl < 0x7ffffc00LL ? sl : 0x7ffffc00LL);
     }
     pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;
     pl.n_rows = (int64_t)B * Sq * Hq;

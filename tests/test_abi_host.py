@@ -153,10 +153,11 @@ def test_decode_rejects(kw, status):
 
 
 def test_workspace_bytes():
-    # paged, 64 sequences x 8 KV heads: 2048-key splits (16 splits of 32768 keys),
-    # (dv + 2) floats per row per split
+    # paged, 64 sequences x 8 KV heads: 6144-key splits (6 splits of 32768 keys), so that
+    # the expected non-empty splits fill one round of wave slots; (dv + 2) floats per row
+    # per split
     n = attn.attn_decode_workspace_bytes(64, 64, 8, 1, 32768, 128, 128)
-    assert n >= 64 * 64 * 16 * 130 * 4
+    assert n == (64 * 64 * 6 * 130 * 4 + 255) // 256 * 256
     # one sequence: 256-key splits keep about 4096 wavefronts busy
     n = attn.attn_decode_workspace_bytes(1, 8, 8, 1, 16384, 128, 128)
     assert n >= 1 * 8 * 64 * 130 * 4
@@ -324,9 +325,9 @@ def test_noalloc_rejects_sizes_past_the_static_scratch():
         return lib.attn_decode_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, 0, 0, 0, B, Hq, 8, Sq, Sk_max, 128, 128,
                                            ctypes.c_float(0.1), 0, ctypes.c_float(0.0), None, FAKE, 64, 512,
                                            FAKE, None, None, None, 0, ctypes.c_int64(0), None, None, None)
-    # 64 sequences x 64 heads x 4 draft tokens of up to 32K keys need 68 MB of partials
-    assert binding.attn_decode_workspace_bytes(64, 64, 8, 4, 32768, 128, 128) > (64 << 20)
-    assert call(64, 64, 4, 32768) == binding.ATTN_ERR_UNSUPPORTED
+    # 256 sequences x 64 heads x 8 draft tokens of up to 32K keys need 68 MB of partials
+    assert binding.attn_decode_workspace_bytes(256, 64, 8, 8, 32768, 128, 128) > (64 << 20)
+    assert call(256, 64, 8, 32768) == binding.ATTN_ERR_UNSUPPORTED
     assert b"static scratch" in lib.attn_last_error()
     # the ordinary argument checks come first
     assert call(0, 64, 1, 32768) == binding.ATTN_ERR_INVALID_ARG

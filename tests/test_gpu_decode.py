@@ -101,34 +101,41 @@ def test_config4_full_size():
     print("config 4, %d elements: max err %.3g cos %.8f" % (ro.size, err, cos))
 
 
-def _planned_split(B, Hq, Hkv, Sq, Sk_max, dk, dv):
-    """Key-split length the library plans, read back from the workspace size
+def _planned_splits(B, Hq, Hkv, Sq, Sk_max, dk, dv):
+    """Number of key splits the library plans, read back from the workspace size
     (rows * n_split * (dv + 2) fp32, rounded up to 256 bytes)."""
     ws = binding.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk_max, dk, dv)
     rows = B * Sq * Hq
     n_split = ws // (rows * (dv + 2) * 4)
-    for sl in (256, 512, 1024, 2048, 4096):
-        if -(-Sk_max // sl) == n_split:
-            return sl
-    raise AssertionError("no split length matches a workspace of %d bytes" % ws)
+    assert ws - n_split * rows * (dv + 2) * 4 < 256, "workspace of %d bytes is not a whole number of splits" % ws
+    return n_split
 
 
 def test_paged_split_lengths_512_1024():
     """Shapes whose (sequence, KV head) count plans 512- and 1024-key splits."""
-    assert _planned_split(8, 16, 8, 1, 20000, 128, 128) == 512
+    assert _planned_splits(8, 16, 8, 1, 20000, 128, 128) == -(-20000 // 512)
     check_paged(8, 16, 8, 128, 128, 9000, 20000, seed=210)
-    assert _planned_split(16, 8, 8, 1, 20000, 64, 64) == 1024
+    assert _planned_splits(16, 8, 8, 1, 20000, 64, 64) == -(-20000 // 1024)
     check_paged(16, 8, 8, 64, 64, 12000, 20000, causal=True, Sq=1, o_dtype="bf16", seed=211)
-    assert _planned_split(16, 64, 8, 2, 20000, 64, 64) == 1024      # 16 columns per KV head
+    assert _planned_splits(16, 64, 8, 2, 20000, 64, 64) == -(-20000 // 1024)      # 16 columns per KV head
     check_paged(16, 64, 8, 64, 64, 15000, 20000, Sq=2, causal=True, seed=212)
 
 
-def test_config4_shape_draft_tokens_4096_key_splits():
+def test_paged_split_length_3072():
+    """A split length that is a multiple of 1024 but not a power of two (3072 keys: 7
+    splits of 20000 keys for 48 sequences x 8 KV heads), sequences ending inside, at and
+    just past a split boundary."""
+    assert _planned_splits(48, 16, 8, 1, 20000, 128, 128) == -(-20000 // 3072)
+    lens = np.array([3072, 3073, 6144, 6143, 20000, 1, 9215, 9216, 12289, 17000, 33, 3071] * 4, np.int32)
+    check_paged(48, 16, 8, 128, 128, 1, 20000, seed=213, lens=lens)
+
+
+def test_config4_shape_draft_tokens_6144_key_splits():
     """The workload's shape with 4 causal draft tokens per sequence: 32 query columns per KV
-    head take the 32-column instance and 4096-key splits. Sequences of the longest,
+    head take the 32-column instance and 6144-key splits. Sequences of the longest,
     shortest and a few other lengths are compared with the oracle."""
     c = synth.CONFIGS["c4_paged_gqa_decode"]
-    assert _planned_split(c["B"], c["Hq"], c["Hkv"], 4, c["len_hi"], c["dk"], c["dv"]) == 4096
+    assert _planned_splits(c["B"], c["Hq"], c["Hkv"], 4, c["len_hi"], c["dk"], c["dv"]) == -(-c["len_hi"] // 6144)
     print("config 4 shape, 4 draft tokens, causal", flush=True)
     case = synth.paged_case(c["seed"], c["B"], c["Hq"], c["Hkv"], c["dk"], c["dv"], c["len_lo"], c["len_hi"],
                             block_size=c["block_size"], Sq=4)

@@ -71,7 +71,7 @@ def test_noalloc_gathered_two_calls_second_smaller():
 def test_noalloc_rejects_past_the_scratch_and_leaves_outputs():
     """A call that needs more than the static scratch is refused with ATTN_ERR_UNSUPPORTED
     and enqueues nothing (the output keeps its contents)."""
-    B, Hq, Hkv, Sq, hi, d = 64, 64, 8, 4, 32768, 128
+    B, Hq, Hkv, Sq, hi, d = 256, 64, 8, 8, 32768, 128
     assert binding.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, hi, d, d) > (64 << 20)
     q = torch.zeros((B, Sq, Hq, d), device="cuda", dtype=torch.bfloat16)
     kc = torch.zeros((4, Hkv, 64, d), device="cuda", dtype=torch.bfloat16)
