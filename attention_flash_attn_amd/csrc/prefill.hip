@@ -71,6 +71,19 @@ struct PrefillParams {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
+
+// Buffer -> LDS copy of 16 bytes per lane as inline assembly, which the compiler does not
+// track. Tracked copies of the next tile made the compiler wait for every copy in flight
+// before the first transposing V^T read of the current tile (it cannot tell the two stages
+// apart), so a tile's copies had only its QK product and softmax to land in. The kernel waits
+// for its copies itself (vmcnt(0), then the workgroup barrier) before any read of their
+// stage. No output registers; M0 carries the LDS address.
+__device__ __forceinline__ void buffer_load_lds16_u(i32x4 rsrc, uint32_t voffset, void* lds_base) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_base));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 : : "v"(voffset), "s"(rsrc), "s"(m) : "m0");
+}
+
 constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
 
 // LDS fragment reads issued ahead of their MFMA (K: 128-bit reads, V: transposing pairs)
@@ -109,6 +122,20 @@ void prefill_kernel(PrefillParams p) {
     constexpr int KSEG = K_BYTES / 1024, VSEG = V_BYTES / 1024;  // 1 KB load segments per tile
     static_assert(DK % 16 == 0 && DV % 16 == 0 && BN % 32 == 0, "tile shape");
     static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "tile must split into 1 KB segments");
+
+    // Copies of the next tile untracked by the compiler (head dims <= 128; see
+    // buffer_load_lds16_u): with the tile's whole period to land in, the causal prefill at
+    // B=2, H=32, 4096^2, d=128 ran 282-286 us against 299-311 us after a 2 GiB cache flush, and
+    // 264 against 266-270 us warm. At d = 256 the tracked form was 1.8% faster (GQA 64:8,
+    // 4096^2: 912 against 928 us, warm): there the compiler's wait keeps the next tile's LDS
+    // writes clear of the PV product's fragment reads.
+    constexpr bool UNTRACKED = DK <= 128;
+    auto copy16 = [](i32x4 rsrc, uint32_t voffset, void* lds) {
+        if constexpr (UNTRACKED)
+            buffer_load_lds16_u(rsrc, voffset, lds);
+        else
+            buffer_load_lds16(rsrc, voffset, lds);
+    };
 
     // additive mask (ADDM): each wave's 32 query rows x BN keys of fp16 per stage
     constexpr int MT = 32 * BN * 2;
@@ -186,7 +213,7 @@ void prefill_kernel(PrefillParams p) {
                 const int kk = s / SEGK;
                 const int r = (s % SEGK) * 32 + (lane >> 1);
                 const int piece = (lane & 1) ^ ((r >> 3) & 1);
-                buffer_load_lds16(krsrc, kbase_off + (uint32_t)(r * kstride * 2 + kk * 32 + piece * 16),
+                copy16(krsrc, kbase_off + (uint32_t)(r * kstride * 2 + kk * 32 + piece * 16),
                                   sb + s * 1024);
             }
         }
@@ -200,7 +227,7 @@ void prefill_kernel(PrefillParams p) {
                 const uint32_t vo = (db * 32 + q * 8 < DV)
                                         ? vbase_off + (uint32_t)(r * vstride * 2 + db * 64 + q * 16)
                                         : kOobOffset;
-                buffer_load_lds16(vrsrc, vo, sb + K_BYTES + s * 1024);
+                copy16(vrsrc, vo, sb + K_BYTES + s * 1024);
             }
         }
     };
@@ -217,6 +244,12 @@ void prefill_kernel(PrefillParams p) {
             if (qi < p.Sq) qf[kk] = load_q8<F16>(p.q, qrow + (2 * kk + half) * 8, p.q_type);
         }
     }
+
+    // The query fragments must have landed before the tile loops: otherwise the compiler, unable
+    // to tell across the back edge whether their loads completed, waits for every load in flight
+    // (the next tile's untracked copies included) at their first use in every tile.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(qf[kk]));
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -257,7 +290,7 @@ void prefill_kernel(PrefillParams p) {
                 const int c = (lane % MCH) ^ mswz(r);
                 const uint32_t off = (uint32_t)((size_t)min(q0 + r, p.Sq - 1) * (size_t)p.mask_stride * 2) +
                                      (uint32_t)(t * BN * 2 + c * 16);
-                buffer_load_lds16(mrsrc, off, mstage + st * NW * MT + j * 1024);
+                copy16(mrsrc, off, mstage + st * NW * MT + j * 1024);
             }
         }
     };
