@@ -43,11 +43,11 @@ _D256_SRC = ("prefill.hip", "prefill_d256.hip", "attn_device.hpp", "../build.py"
 _DECODE_SRC = ("decode.hip", "attn_device.hpp", "../build.py")
 _GATHER_SRC = ("decode.hip", "decode_gathered.hip", "attn_device.hpp", "../build.py")
 MEASURED_TRAFFIC = {
-    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "e8151564efdc1ec2", "bytes": 662746776},
-    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "4293da1dbef2a15f", "bytes": 1342340180},
-    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "4293da1dbef2a15f", "bytes": 352552600},
-    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "2e7f6998c039ad78", "bytes": 5005640602},
-    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "49e4f786e6856375", "bytes": 75627773},
+    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "5b298f72a7586638", "bytes": 511611728},
+    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "e0eb12895867a66a", "bytes": 1342332493},
+    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "e0eb12895867a66a", "bytes": 352557336},
+    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "2e7f6998c039ad78", "bytes": 5005641379},
+    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "49e4f786e6856375", "bytes": 75630574},
 }
 
 
