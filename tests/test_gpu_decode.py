@@ -130,6 +130,15 @@ def test_paged_split_length_3072():
     check_paged(48, 16, 8, 128, 128, 1, 20000, seed=213, lens=lens)
 
 
+def test_paged_draft_tokens_3072_key_splits():
+    """4 causal draft tokens x 8 heads per KV head (the 32-column instance) at 3072-key splits,
+    every output compared: sequences ending inside, at and just past split boundaries, shorter
+    than the draft, and a single key."""
+    assert _planned_splits(48, 64, 8, 4, 20000, 128, 128) == -(-20000 // 3072)
+    lens = np.array([3072, 3075, 6144, 6146, 20000, 1, 9215, 9216, 12289, 17000, 33, 3071] * 4, np.int32)
+    check_paged(48, 64, 8, 128, 128, 1, 20000, Sq=4, causal=True, o_dtype="bf16", seed=214, lens=lens)
+
+
 def test_config4_shape_draft_tokens_6144_key_splits():
     """The workload's shape with 4 causal draft tokens per sequence: 32 query columns per KV
     head take the 32-column instance and 6144-key splits. Sequences of the longest,
