@@ -612,31 +612,49 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
         while (sl < len && sl < 1024) sl <<= 1;
         pl.split_len = sl;
     } else {
-        // paged: one wavefront per (split, KV head, column group, sequence), with 2048 wave
-        // slots on the chip (two waves per SIMD at head dims <= 128, else 1024). A split waits
-        // for a slot only when more splits exist than slots, and such late starters set the
-        // end of the launch, so the splits are made as short as possible while the expected
-        // number of non-empty ones still fits in 90% of the slots. The lengths are device data;
-        // taking them spread evenly up to Sk_max, n splits of a full-length sequence leave
-        // (n + 1) / 2 per sequence on average: units * (n + 1) / 2 <= 0.9 * slots. Split
-        // lengths are powers of two up to 1024 keys and multiples of 1024 above.
-        // Measured at 64 sequences of 1024..32768 keys, 8 KV heads, d = 128 (one KV-head
-        // column group), split lengths against time per call:
-        //   one token:      2048: 853-857 us, 3072: 838, 4096: 863, 5120: 922, 6144: 814
-        //   4 draft tokens: 3072: 925, 4096: 928-938, 5120: 975, 6144: 868-870, 7168: 937,
-        //                   8192: 987
-        // This rule picks 6 splits (6144 keys) there: 231 of each XCD's 256 slots.
+        // paged: one wavefront per (split, KV head, column group, sequence).
         const long long nq = (long long)Sq * (Hkv > 0 ? Hq / Hkv : 1);
-        const long long cols = paged_cols(dk, (int)(nq < (1 << 30) ? nq : (1 << 30)));
-        long long units = (long long)B * Hkv * ((nq + cols - 1) / cols);
-        if (units < 1) units = 1;
-        const long long slots = dk <= 128 ? 2048 : 1024;
-        long long n = (18 * slots / units - 10) / 10;  // floor(1.8 * slots / units - 1)
-        if (n < 1) n = 1;
-        const long long len = Sk_max > 0 ? (Sk_max + n - 1) / n : 256;
-        long long sl = 256;
-        while (sl < len && sl < 1024) sl <<= 1;
-        if (sl < len) sl = (len + 1023) / 1024 * 1024;
+        const int cols = paged_cols(dk, (int)(nq < (1 << 30) ? nq : (1 << 30)));
+        long long sl;
+        if (dk <= 128 && Sk_max >= 16384) {
+            // Long contexts at two waves per SIMD (2048 wave slots on the chip): a split that
+            // finds no free slot starts late, and late starters set the end of the launch, so
+            // the splits are made as short as possible while the expected number of non-empty
+            // ones still fits in 90% of the slots. The lengths are device data; taking them
+            // spread evenly up to Sk_max, n splits of a full-length sequence leave (n + 1) / 2
+            // per sequence on average: units * (n + 1) / 2 <= 0.9 * slots. Split lengths are
+            // powers of two up to 1024 keys and multiples of 1024 above.
+            // Measured at 64 sequences of 1024..32768 keys, 8 KV heads, d = 128 (one column
+            // group), split length against time per call:
+            //   one token:      2048: 853-857 us, 3072: 838, 4096: 863, 5120: 922, 6144: 814
+            //   4 draft tokens: 3072: 925, 4096: 928-938, 5120: 975, 6144: 868-870, 7168: 937,
+            //                   8192: 987
+            // (this rule picks 6 splits, 6144 keys: 231 of each XCD's 256 slots), and against
+            // the rule below at 8 sequences of 16K..32K keys 158 vs 163 us, 16 of 1K..32K 215 vs
+            // 222 us.
+            long long units = (long long)B * Hkv * ((nq + cols - 1) / cols);
+            if (units < 1) units = 1;
+            const long long slots = 2048;
+            long long n = (18 * slots / units - 10) / 10;  // floor(1.8 * slots / units - 1)
+            if (n < 1) n = 1;
+            const long long len = (Sk_max + n - 1) / n;
+            sl = 256;
+            while (sl < len && sl < 1024) sl <<= 1;
+            if (sl < len) sl = (len + 1023) / 1024 * 1024;
+        } else {
+            // Shorter contexts, and head dims above 128 (one wave per SIMD): about 4096
+            // wavefronts (B * Hkv * splits), splits of 256..2048 keys (4096 with 32-column
+            // groups, whose fp32 partials are twice as large). Against the rule above this was
+            // faster at 64 sequences of 1K..8K keys: d = 256 436 vs 455 us, d = 192 335 vs 346,
+            // d = 64 with 4 draft tokens 139 vs 141, and at 128 sequences of 512..4096 keys
+            // (32:8 heads, d = 128) 229 vs 238 us.
+            const long long pairs = (long long)B * Hkv;
+            const long long want = (4096 + pairs - 1) / (pairs > 0 ? pairs : 1);
+            const long long len = Sk_max > 0 ? (Sk_max + want - 1) / want : 256;
+            const long long max_sl = cols == 32 ? 4096 : 2048;
+            sl = 256;
+            while (sl < len && sl < max_sl) sl <<= 1;
+        }
         pl.split_len = (int)(sl < 0x7ffffc00LL ? sl : 0x7ffffc00LL);
     }
     pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;
