@@ -140,7 +140,8 @@ attn_status attn_prefill_fwd_ex(const void* q, int q_dtype, const void* k, const
 
 /*
  * Workspace (bytes) that attn_decode_fwd needs for these sizes: the split-KV
- * partial results (fp32 output rows plus running max and sum per split).
+ * partial results (paged: fp32 output rows; gathered: bf16 output rows divided
+ * by their own sum; plus the running max and sum per row and split).
  * Sk_max is the largest sequence length (paged mode) or n_sel (gathered mode).
  * Returns 0 for sizes that attn_decode_fwd would reject in either mode (invalid,
  * or past the mode-independent launch-size limits below).
@@ -157,8 +158,11 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk_max, i
  * token's, the token's own row as one more key) and its Notes (the tokens of a
  * call batched into the matrix products). The keys are split into
  * fixed-size ranges processed in parallel, then merged by log-sum-exp. The
- * range length (paged 256..4096 keys, gathered 64..1024) depends only on the
- * sizes passed here and to attn_decode_workspace_bytes. Launch-size limits
+ * range length depends only on the sizes passed here and to
+ * attn_decode_workspace_bytes: gathered 64..1024 keys; paged 256..4096 keys, or,
+ * for Sk_max >= 16384 at head dims up to 128, the shortest power of two up to
+ * 1024 or multiple of 1024 keys whose expected number of non-empty ranges
+ * (lengths taken spread up to Sk_max) fills the GPU's wave slots about once. Launch-size limits
  * (ATTN_ERR_UNSUPPORTED past them): B and the number of ranges at most 65535
  * each; B * Sq * Hq under 2^26 output rows; paged mode
  * Hkv * ceil(Sq * (Hq / Hkv) / 16) under 2^26; gathered mode
