@@ -126,10 +126,14 @@ void prefill_kernel(PrefillParams p) {
     // Copies of the next tile untracked by the compiler (head dims <= 128; see
     // buffer_load_lds16_u): with the tile's whole period to land in, the causal prefill at
     // B=2, H=32, 4096^2, d=128 ran 282-286 us against 299-311 us after a 2 GiB cache flush, and
-    // 264 against 266-270 us warm. At d = 256 the tracked form was 1.8% faster (GQA 64:8,
-    // 4096^2: 912 against 928 us, warm): there the compiler's wait keeps the next tile's LDS
-    // writes clear of the PV product's fragment reads.
-    constexpr bool UNTRACKED = DK <= 128;
+    // 264 against 266-270 us warm. At d = 256 untracked copies issued at the top of the tile were
+    // 1.8% slower (GQA 64:8, 4096^2: 928 against 912 us, warm): their LDS writes then meet the
+    // fragment reads. Without the causal mask, d = 256 issues them untracked after the QK product
+    // instead (LATE), so they land during the softmax: 931-936 against 940-947 us; the causal
+    // instances keep the tracked form (with LATE 555-559 against 548-550 us), and so do the
+    // masked ones (not measured with LATE).
+    constexpr bool LATE = DK == 256 && !CAUSAL && !ADDM;
+    constexpr bool UNTRACKED = DK <= 128 || LATE;
     auto copy16 = [](i32x4 rsrc, uint32_t voffset, void* lds) {
         if constexpr (UNTRACKED)
             buffer_load_lds16_u(rsrc, voffset, lds);
@@ -301,7 +305,7 @@ void prefill_kernel(PrefillParams p) {
     const int kofs = col * 32 + ((half ^ ((col >> 3) & 1)) << 4);
     const int vofs = (half * 4 + ((lane & 15) >> 2)) * 64 + (((lane >> 4) & 1) * 16 + (lane & 3) * 4) * 2;
 
-    auto tile = [&](const char* kt, const char* vt, const char* mt, int key0, auto mask_tag) {
+    auto tile = [&](const char* kt, const char* vt, const char* mt, int key0, auto mask_tag, auto&& post_qk) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // S^T = K Q^T; K fragments are read from LDS PF steps ahead of their MFMA
         constexpr int NQK = KB * KK;
@@ -321,6 +325,10 @@ void prefill_kernel(PrefillParams p) {
             const bf16x8 a = kring[idx % PFK];
             if (idx + PFK < NQK) kring[idx % PFK] = kload(idx + PFK);
             sacc[idx / KK] = mma32<F16>(a, qf[idx % KK], sacc[idx / KK]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (LATE) {
+            post_qk();
             __builtin_amdgcn_sched_barrier(0);
         }
         // scores in log2 units (softcap) or raw (scaled inside the exponent), mask, tile max.
@@ -434,24 +442,33 @@ void prefill_kernel(PrefillParams p) {
     auto step = [&](int t) {
         wait_vmem();       // this wave's copies of tile t (K/V and its mask rows) have landed
         __syncthreads();   // ... and every other wave's; stage (t+1)&1 is free again
-        if (t + 1 < ntiles) {
+        if (!LATE && t + 1 < ntiles) {
             issue(t + 1, (t + 1) & 1);
             mload(t + 1, (t + 1) & 1);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
+    auto late = [&](int t) {  // LATE: the next tile's copies, issued after the QK product
+        if (LATE && t + 1 < ntiles) {
+            issue(t + 1, (t + 1) & 1);
+            mload(t + 1, (t + 1) & 1);
+        }
+    };
 #pragma clang loop unroll(disable)
     for (int t = 0; t < t_full; ++t) {
         step(t);
         const char* kt = smem + (t & 1) * STAGE;
-        tile(kt, kt + K_BYTES, mstage + (t & 1) * NW * MT, t * BN, std::false_type{});
+        tile(kt, kt + K_BYTES, mstage + (t & 1) * NW * MT, t * BN, std::false_type{}, [&]() { late(t); });
     }
 #pragma clang loop unroll(disable)
     for (int t = t_full; t < ntiles; ++t) {
         step(t);
         const char* kt = smem + (t & 1) * STAGE;
         const bool skip = CAUSAL && (t * BN > q0 + 31 + shift);  // wave-uniform
-        if (!skip) tile(kt, kt + K_BYTES, mstage + (t & 1) * NW * MT, t * BN, std::true_type{});
+        if (!skip)
+            tile(kt, kt + K_BYTES, mstage + (t & 1) * NW * MT, t * BN, std::true_type{}, [&]() { late(t); });
+        else
+            late(t);
     }
 
     // epilogue: sinks, normalisation, store
