@@ -657,7 +657,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Sq, int Sk_max, int dk, int d
         }
         pl.split_len = (int)(sl < 0x7ffffc00LL ? sl : 0x7ffffc00LL);
     }
-    pl.n_split = Sk_max > 0 ? (Sk_max + pl.split_len - 1) / pl.split_len : 1;
+    pl.n_split = Sk_max > 0 ? (int)(((long long)Sk_max + pl.split_len - 1) / pl.split_len) : 1;
     pl.n_rows = (int64_t)B * Sq * Hq;
     // partial rows (fp32 O_s, or bf16 O_s / l_s for gathered rows), then (max, sum) per row and split
     pl.ws_bytes = (size_t)pl.n_rows * pl.n_split * ((size_t)dv * (gathered ? 2 : 4) + 2 * sizeof(float));

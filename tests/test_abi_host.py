@@ -166,6 +166,11 @@ def test_workspace_bytes():
     n = attn.attn_decode_workspace_bytes(16, 128, 1, 1, 2048, 576, 512)
     assert n == (16 * 128 * 8 * (512 * 2 + 8) + 255) // 256 * 256
     assert attn.attn_decode_workspace_bytes(0, 64, 8, 1, 100, 128, 128) == 0
+    # the longest key count an int holds: a whole number of splits, at most 65535 of them
+    n = attn.attn_decode_workspace_bytes(1, 8, 8, 1, 2**31 - 1, 128, 128)
+    row_split = 8 * 130 * 4
+    assert 0 < n and (n // row_split) * row_split <= n < (n // row_split) * row_split + 256
+    assert 1 <= n // row_split <= 65535
     assert attn.attn_decode_workspace_bytes(2, 6, 4, 1, 100, 128, 128) == 0
     # past the launch limits (2^26 output rows; B above 65535): no workspace size
     assert attn.attn_decode_workspace_bytes(1024, 1 << 16, 1 << 16, 1, 100, 128, 128) == 0
