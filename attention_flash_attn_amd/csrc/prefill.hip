@@ -71,7 +71,6 @@ struct PrefillParams {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-
 // Buffer -> LDS copy of 16 bytes per lane as inline assembly, which the compiler does not
 // track. Tracked copies of the next tile made the compiler wait for every copy in flight
 // before the first transposing V^T read of the current tile (it cannot tell the two stages
@@ -123,15 +122,15 @@ void prefill_kernel(PrefillParams p) {
     static_assert(DK % 16 == 0 && DV % 16 == 0 && BN % 32 == 0, "tile shape");
     static_assert(K_BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "tile must split into 1 KB segments");
 
-    // Copies of the next tile untracked by the compiler (head dims <= 128; see
-    // buffer_load_lds16_u): with the tile's whole period to land in, the causal prefill at
-    // B=2, H=32, 4096^2, d=128 ran 282-286 us against 299-311 us after a 2 GiB cache flush, and
-    // 264 against 266-270 us warm. At d = 256 untracked copies issued at the top of the tile were
-    // 1.8% slower (GQA 64:8, 4096^2: 928 against 912 us, warm): their LDS writes then meet the
-    // fragment reads. Without the causal mask, d = 256 issues them untracked after the QK product
-    // instead (LATE), so they land during the softmax: 931-936 against 940-947 us; the causal
-    // instances keep the tracked form (with LATE 555-559 against 548-550 us), and so do the
-    // masked ones (not measured with LATE).
+    // Copies of the next tile untracked by the compiler (head dims <= 128, and d = 256 without
+    // masks; see buffer_load_lds16_u). At d <= 128, with the tile's whole period to land in,
+    // the causal prefill at B=2, H=32, 4096^2, d=128 ran 282-286 us against 299-311 us after a
+    // 2 GiB cache flush, and 264 against 266-270 us warm. At d = 256 untracked copies issued at
+    // the top of the tile were 1.8% slower (GQA 64:8, 4096^2: 928 against 912 us, warm): their
+    // LDS writes then meet the fragment reads. Without the causal mask, d = 256 issues them
+    // untracked after the QK product instead (LATE), so they land during the softmax: 931-936
+    // against 940-947 us; the causal instances keep the tracked form (with LATE 555-559 against
+    // 548-550 us), and so do the masked ones (not measured with LATE).
     constexpr bool LATE = DK == 256 && !CAUSAL && !ADDM;
     constexpr bool UNTRACKED = DK <= 128 || LATE;
     auto copy16 = [](i32x4 rsrc, uint32_t voffset, void* lds) {
@@ -217,8 +216,7 @@ void prefill_kernel(PrefillParams p) {
                 const int kk = s / SEGK;
                 const int r = (s % SEGK) * 32 + (lane >> 1);
                 const int piece = (lane & 1) ^ ((r >> 3) & 1);
-                copy16(krsrc, kbase_off + (uint32_t)(r * kstride * 2 + kk * 32 + piece * 16),
-                                  sb + s * 1024);
+                copy16(krsrc, kbase_off + (uint32_t)(r * kstride * 2 + kk * 32 + piece * 16), sb + s * 1024);
             }
         }
 #pragma unroll
