@@ -561,9 +561,14 @@ PrefillParams make_params(const PrefillArgs& a) {
     p.c_tanh = softcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
     p.c_cap = a.softcap * kLog2e;
     p.xcd_remap = ((a.B * a.Hq) % 8) == 0;
-    // grouped query heads per XCD: measured 3.5% faster for causal GQA at d=256, 2.4% slower
-    // without the causal mask
-    if (a.causal && a.Hq != a.Hkv && ((a.B * a.Hkv) % 8) == 0) p.xcd_remap = 2;
+    // grouped query heads per XCD: measured 3.5% faster for causal GQA at d=256. Without the
+    // causal mask it was 2.4% slower while the tile copies were tracked; with the d = 256
+    // unmasked kernel's copies issued untracked after the QK product it measured 1-2% faster
+    // back to back (GQA 64:8, 4096^2: 865.6-877.9 against 874.5-894.5 us, same process, 8
+    // rounds) and the same within 0.2% in the benchmark's sequence (894-896 us), so it applies
+    // there too. Other head dims without the causal mask keep the heads spread (not measured).
+    const bool late_copies = a.dk == 256 && a.dv == 256 && !a.causal && a.mask == nullptr;
+    if ((a.causal || late_copies) && a.Hq != a.Hkv && ((a.B * a.Hkv) % 8) == 0) p.xcd_remap = 2;
     p.mask = (const uint16_t*)a.mask;
     p.mask_stride = a.mask_stride;
     p.mask_batch = a.mask_batch;
