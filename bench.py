@@ -43,11 +43,11 @@ _D256_SRC = ("prefill.hip", "prefill_d256.hip", "attn_device.hpp", "../build.py"
 _DECODE_SRC = ("decode.hip", "attn_device.hpp", "../build.py")
 _GATHER_SRC = ("decode.hip", "decode_gathered.hip", "attn_device.hpp", "../build.py")
 MEASURED_TRAFFIC = {
-    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "575c903da65417f2", "bytes": 513116702},
-    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "734201b12eff8024", "bytes": 402870530},
-    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "734201b12eff8024", "bytes": 352556442},
-    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "6edd13a4fc5570a2", "bytes": 5005636705},
-    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "8ab14e5d4fcc8d7d", "bytes": 75632091},
+    "c2_causal_mha_d128": {"sources": _PREFILL_SRC, "sha256_16": "575c903da65417f2", "bytes": 516715207},
+    "c3a_gqa_d256": {"sources": _D256_SRC, "sha256_16": "734201b12eff8024", "bytes": 402870613},
+    "c3b_gqa_d256_causal_softcap": {"sources": _D256_SRC, "sha256_16": "734201b12eff8024", "bytes": 352557191},
+    "c4_paged_gqa_decode": {"sources": _DECODE_SRC, "sha256_16": "75c2b117ce424e09", "bytes": 5005640975},
+    "c5_gathered_mla_decode": {"sources": _GATHER_SRC, "sha256_16": "d8da7d1a4dfd9d5e", "bytes": 75633897},
 }
 
 
